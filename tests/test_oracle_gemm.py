@@ -1,0 +1,140 @@
+"""Pins for the oracle's block-scaled GEMM and grouped GEMM (CPU only).
+
+Pinned against: exact rational arithmetic (Fractions) on tiny shapes, an
+independent int64 evaluation of every chunk partial, the K = 128 special case,
+a torch float64 matmul when all scales are 1, linearity in one scale, and the
+flushed-group rule.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import workloads
+from oracle import e4m3, gemm, quant
+
+
+def _quantized(M, N, K, seed, mode="f32"):
+    rng = np.random.default_rng(seed)
+    A = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    W = workloads.bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    qa, sa = quant.quantize_act(A, mode)
+    qw, sw = quant.quantize_weight(W, mode)
+    return qa, sa, qw, sw
+
+
+def test_exact_rational_bruteforce():
+    qa, sa, qw, sw = _quantized(6, 128, 384, 1)
+    C = gemm.gemm(qa, sa, qw, sw)
+    bound = gemm.abs_bound(qa, sa, qw, sw)
+    dec = [Fraction(float(v)) if np.isfinite(v) else None for v in e4m3.DECODE_TABLE]
+    for m in range(6):
+        for n in (0, 1, 77, 127):
+            exact = Fraction(0)
+            for k in range(384):
+                g = k // 128
+                exact += (Fraction(float(sa[g, m])) * Fraction(float(sw[n // 128, g]))
+                          * dec[qa[m, k]] * dec[qw[n, k]])
+            # one float64 rounding per chunk add: at most 3 * 2^-53 of the bound
+            assert abs(Fraction(float(C[m, n])) - exact) <= Fraction(float(bound[m, n])) * Fraction(4, 2**53)
+
+
+def test_chunk_partials_exact_against_int64():
+    qa, sa, qw, sw = _quantized(33, 256, 512, 2)
+    ia = (e4m3.decode(qa) * 512).astype(np.int64)
+    iw = (e4m3.decode(qw) * 512).astype(np.int64)
+    for g, P in gemm.chunk_partials(qa, qw):
+        ks = slice(g * 128, (g + 1) * 128)
+        Pi = ia[:, ks] @ iw[:, ks].T  # integer, units of 2^-18
+        assert np.array_equal(P, np.ldexp(Pi.astype(np.float64), -18))
+        assert np.all(np.abs(Pi) < 2**53)
+
+
+def test_k128_reduces_to_scaled_product():
+    qa, sa, qw, sw = _quantized(17, 256, 128, 3)
+    C = gemm.gemm(qa, sa, qw, sw)
+    A = e4m3.decode(qa)
+    W = e4m3.decode(qw)
+    ref = sa[0].astype(np.float64)[:, None] * np.repeat(sw[:, 0].astype(np.float64), 128)[None, :] * (A @ W.T)
+    assert np.array_equal(C, ref)
+
+
+def test_unit_scales_match_torch_matmul():
+    qa, _, qw, _ = _quantized(40, 128, 640, 4)
+    sa = np.ones((5, 40), np.float32)
+    sw = np.ones((1, 5), np.float32)
+    C = gemm.gemm(qa, sa, qw, sw)
+    ref = (torch.from_numpy(qa).view(torch.float8_e4m3fn).to(torch.float64)
+           @ torch.from_numpy(qw).view(torch.float8_e4m3fn).to(torch.float64).T).numpy()
+    assert np.array_equal(C, ref)
+
+
+def test_linear_in_one_group_scale_and_flushed_group():
+    qa, sa, qw, sw = _quantized(8, 128, 512, 5)
+    C = gemm.gemm(qa, sa, qw, sw)
+    A = e4m3.decode(qa)
+    W = e4m3.decode(qw)
+    g, m = 2, 3
+    contrib = float(sa[g, m]) * float(sw[0, g]) * (A[m, 256:384] @ W[:, 256:384].T)
+    sa2 = sa.copy()
+    sa2[g, m] *= 2
+    C2 = gemm.gemm(qa, sa2, qw, sw)
+    assert np.allclose(C2[m] - C[m], contrib, rtol=0, atol=1e-12 * np.abs(C[m]).max())
+    others = np.arange(8) != m
+    assert np.array_equal(C2[others], C[others])
+    # a flushed activation group (codes zero, scale zero) contributes nothing
+    qa3, sa3 = qa.copy(), sa.copy()
+    qa3[m, 256:384] = 0
+    sa3[g, m] = 0
+    C3 = gemm.gemm(qa3, sa3, qw, sw)
+    assert np.allclose(C3[m], C[m] - contrib, rtol=0, atol=1e-12 * np.abs(C[m]).max())
+
+
+def test_sign_and_transpose_sensitivity():
+    """Swapping operand roles transposes the output; negating A negates C."""
+    qa, sa, qw, sw = _quantized(128, 128, 256, 6)
+    C = gemm.gemm(qa, sa, qw, sw)
+    # W's block scales, spread over its 128 rows, serve as activation scales
+    sa_blk = np.repeat(sw[0][:, None], 128, axis=1)  # [K/128][M=128]
+    Ct = gemm.gemm(qw, sa_blk, qa, np.ones((1, 2), np.float32))
+    Cr = gemm.gemm(qa, np.ones_like(sa), qw, sw)
+    assert np.array_equal(Ct.T, Cr)
+    Cn = gemm.gemm(qa ^ np.uint8(0x80), sa, qw, sw)
+    assert np.array_equal(Cn, -C)
+
+
+def test_grouped_equals_per_expert_dense():
+    rng = np.random.default_rng(8)
+    G, N, K = 5, 128, 256
+    counts = np.array([3, 0, 17, 1, 0])
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(counts)
+    Mt = int(off[-1]) + 4  # rows past off[G] are not part of the result
+    A = workloads.bf16_bits(rng.standard_normal((Mt, K)).astype(np.float32))
+    qa, sa = quant.quantize_act(A)
+    qws, sws = [], []
+    for e in range(G):
+        W = workloads.bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+        q, s = quant.quantize_weight(W)
+        qws.append(q)
+        sws.append(s)
+    qw, sw = np.stack(qws), np.stack(sws)
+    C = gemm.grouped_gemm(qa, sa, off, qw, sw)
+    for e in range(G):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            assert np.array_equal(C[r0:r1], gemm.gemm(qa[r0:r1], sa[:, r0:r1], qw[e], sw[e]))
+    assert np.all(np.isnan(C[off[-1]:]))
+
+
+def test_bf16_rounding_helpers():
+    v = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -3.0 - 2.0 ** -7, 1e-3])
+    r = gemm.round_to_bf16(v)
+    assert r[0] == 1.0
+    assert r[1] == 1.0  # tie -> even
+    assert r[2] == 1.0 + 2 * 2.0 ** -7  # tie -> even (up)
+    assert r[3] == -3.0  # -3 - 2^-7: half ulp at 2 is 2^-7 -> tie -> even (-3.0)
+    ref = torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(r, ref)
+    assert gemm.bf16_half_ulp(np.array([1.0]))[0] == 2.0 ** -8
