@@ -1,0 +1,158 @@
+// C ABI of libfp8q: host-side validation and launch (declared in include/fp8q.h).
+//
+// Validation runs entirely on the host and before any HIP call, in the order
+// the header documents, so every error path can be exercised without a GPU.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "fp8q.h"
+
+namespace fp8q {
+hipError_t launch_quantize_act(const void* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                               int mode, hipStream_t stream);
+hipError_t launch_quantize_weight(const void* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                                  int mode, hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
+                       const float* w_s, int64_t M, int64_t N, int64_t K, void* c, int out_bf16,
+                       hipStream_t stream);
+hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                               const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
+                               int64_t N, int64_t K, void* c, int out_bf16, hipStream_t stream);
+}  // namespace fp8q
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_cache[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The current device must be a gfx950.  Cached per device ordinal.
+fp8q_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return FP8Q_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int c = g_arch_cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return FP8Q_OK;
+    if (c == 2) return FP8Q_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8Q_ERR_DEVICE;
+  }
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? FP8Q_OK : FP8Q_ERR_DEVICE;
+}
+
+fp8q_status launched(hipError_t e) {
+  if (e == hipSuccess) return FP8Q_OK;
+  (void)hipGetLastError();
+  return FP8Q_ERR_LAUNCH;
+}
+
+bool valid_mode(int m) { return m == FP8Q_SCALE_F32 || m == FP8Q_SCALE_POW2; }
+bool valid_out(int o) { return o == FP8Q_OUT_F32 || o == FP8Q_OUT_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+const char* fp8q_status_string(fp8q_status st) {
+  switch (st) {
+    case FP8Q_OK: return "FP8Q_OK";
+    case FP8Q_ERR_NULL: return "FP8Q_ERR_NULL: a required pointer is NULL";
+    case FP8Q_ERR_SHAPE:
+      return "FP8Q_ERR_SHAPE: negative size, K or N not a multiple of 128, or G < 1";
+    case FP8Q_ERR_ALIGN:
+      return "FP8Q_ERR_ALIGN: data pointer not 16-byte aligned or scale/offset pointer not "
+             "4-byte aligned";
+    case FP8Q_ERR_ENUM: return "FP8Q_ERR_ENUM: unknown scale mode or output dtype";
+    case FP8Q_ERR_DEVICE: return "FP8Q_ERR_DEVICE: no current HIP device, or it is not gfx950";
+    case FP8Q_ERR_LAUNCH: return "FP8Q_ERR_LAUNCH: kernel launch failed";
+    case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: not implemented in this build";
+  }
+  return "FP8Q_ERR_UNKNOWN: not a status code";
+}
+
+fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t M, int64_t K, uint8_t* q, float* s,
+                              fp8q_scale_mode mode, hipStream_t stream) {
+  const bool empty = (M == 0 || K == 0);
+  if (!empty && (!x_bf16 || !q || !s)) return FP8Q_ERR_NULL;
+  if (M < 0 || K < 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8Q_ERR_ALIGN;
+  if (!valid_mode(mode)) return FP8Q_ERR_ENUM;
+  if (empty) return FP8Q_OK;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_quantize_act(x_bf16, M, K, q, s, (int)mode, stream));
+}
+
+fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, uint8_t* q, float* s,
+                                 fp8q_scale_mode mode, hipStream_t stream) {
+  const bool empty = (N == 0 || K == 0);
+  if (!empty && (!w_bf16 || !q || !s)) return FP8Q_ERR_NULL;
+  if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(q, 16) || !aligned(s, 4)) return FP8Q_ERR_ALIGN;
+  if (!valid_mode(mode)) return FP8Q_ERR_ENUM;
+  if (empty) return FP8Q_OK;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_quantize_weight(w_bf16, N, K, q, s, (int)mode, stream));
+}
+
+fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
+                      const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
+                      fp8q_out_dtype out, hipStream_t stream) {
+  const bool empty_out = (M == 0 || N == 0);
+  const bool empty_k = (K == 0);
+  if (!empty_out && !c) return FP8Q_ERR_NULL;
+  if (!empty_out && !empty_k && (!a_q || !a_s || !w_q || !w_s)) return FP8Q_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(c, 16) || !aligned(a_s, 4) ||
+      !aligned(w_s, 4))
+    return FP8Q_ERR_ALIGN;
+  if (!valid_out(out)) return FP8Q_ERR_ENUM;
+  if (empty_out) return FP8Q_OK;
+  if (empty_k) return FP8Q_ERR_UNSUPPORTED;  // C = 0 would need a fill kernel
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_gemm(a_q, a_s, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16, stream));
+}
+
+fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                              const int32_t* off, int32_t G, const uint8_t* w_q,
+                              const float* w_s, int64_t N, int64_t K, void* c,
+                              fp8q_out_dtype out, hipStream_t stream) {
+  const bool empty_out = (M_total == 0 || N == 0);
+  if (!off) return FP8Q_ERR_NULL;
+  if (!empty_out && !c) return FP8Q_ERR_NULL;
+  if (!empty_out && K != 0 && (!a_q || !a_s || !w_q || !w_s)) return FP8Q_ERR_NULL;
+  if (M_total < 0 || N < 0 || K < 0 || G < 1 || N % 128 != 0 || K % 128 != 0)
+    return FP8Q_ERR_SHAPE;
+  if (G > 1024) return FP8Q_ERR_UNSUPPORTED;
+  if (M_total > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;  // offsets are int32
+  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(c, 16) || !aligned(a_s, 4) ||
+      !aligned(w_s, 4) || !aligned(off, 4))
+    return FP8Q_ERR_ALIGN;
+  if (!valid_out(out)) return FP8Q_ERR_ENUM;
+  if (empty_out) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_UNSUPPORTED;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c,
+                                            out == FP8Q_OUT_BF16, stream));
+}
+
+}  // extern "C"

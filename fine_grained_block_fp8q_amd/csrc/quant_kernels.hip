@@ -1,0 +1,223 @@
+// Online fine-grained quantizers: BF16 -> OCP E4M3 with one scale per 1x128
+// activation group or per 128x128 weight block.
+//
+// Method: the-good.kr free board post 2169793, fine-grained quantization
+// passage (max-abs taken online per 1x128 activation tile / 128x128 weight
+// block, scaling factor derived from it so the max-abs maps to the largest
+// FP8 value, then the cast to FP8); power-of-two scales: why-be.co.kr
+// as_center post 72410 (scaling factors that are integral powers of 2).
+//
+// Both kernels are HBM-streaming: every input byte is read once with 16-byte
+// loads, the group max-abs is reduced in registers (DPP within a 16-lane row
+// for activations, plus LDS across waves for weight blocks), and the codes are
+// written with 8-byte stores, 128 contiguous bytes per group row.
+//
+// Arithmetic (bit-exact contract): FP32 mode computes inv = 448/amax and
+// s = amax/448 with IEEE-correct division (this file is built without fast
+// math and without FP contraction), then code = cvt_e4m3_rne(x * inv).  A
+// non-finite inv flushes the group: s = 0 and x * 0 = signed zero.  Pow2 mode
+// scales by an exact ldexp.
+
+#include "fp8q_device.hpp"
+
+namespace fp8q {
+
+struct GroupRule {
+  float mul;   // FP32 mode: x * mul
+  int neg_e;   // pow2 mode: ldexp(x, neg_e)
+  float s;     // stored dequantization scale
+};
+
+// Smallest e with 448 * 2^e >= a (a > 0, finite), from the bits of a.
+// a = f * 2^E with f in [1, 2); 448 = 1.75 * 2^8, so e = E - 8 if f <= 1.75
+// and e = E - 7 otherwise.
+__device__ __forceinline__ int pow2_exponent(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int ef = (int)(b >> 23);
+  uint32_t man = b & 0x7FFFFFu;
+  int E;
+  if (ef != 0) {
+    E = ef - 127;
+  } else {  // FP32 subnormal (a BF16 subnormal widened): a = man * 2^-149
+    const int p = 31 - __clz(man);
+    E = p - 149;
+    man = (man << (23 - p)) & 0x7FFFFFu;
+  }
+  return (man <= 0x600000u) ? E - 8 : E - 7;
+}
+
+__device__ __forceinline__ float exp2_int(int e) {  // 2^e for e in [-149, 127]
+  return (e >= -126) ? __uint_as_float((uint32_t)(e + 127) << 23)
+                     : __uint_as_float(1u << (e + 149));
+}
+
+template <int MODE>
+__device__ __forceinline__ GroupRule group_rule(float amax) {
+  GroupRule r;
+  if (MODE == 0) {
+    const float inv = kE4M3Max / amax;
+    const bool flushed = !__builtin_isfinite(inv);
+    r.mul = flushed ? 0.0f : inv;
+    r.s = flushed ? 0.0f : amax / kE4M3Max;
+    r.neg_e = 0;
+  } else {
+    const int e = (amax > 0.0f) ? pow2_exponent(amax) : 0;
+    r.neg_e = -e;
+    r.s = (amax > 0.0f) ? exp2_int(e) : 0.0f;
+    r.mul = 0.0f;
+  }
+  return r;
+}
+
+template <int MODE>
+__device__ __forceinline__ float apply(float x, const GroupRule& r) {
+  return MODE == 0 ? x * r.mul : __builtin_ldexpf(x, r.neg_e);
+}
+
+// 8 BF16 values (one 16-byte load) -> 8 E4M3 bytes.
+template <int MODE>
+__device__ __forceinline__ uint2 convert8(const uint4 v, const GroupRule& r) {
+  uint2 o;
+  o.x = pack_e4m3x4(apply<MODE>(bf16_lo(v.x), r), apply<MODE>(bf16_hi(v.x), r),
+                    apply<MODE>(bf16_lo(v.y), r), apply<MODE>(bf16_hi(v.y), r));
+  o.y = pack_e4m3x4(apply<MODE>(bf16_lo(v.z), r), apply<MODE>(bf16_hi(v.z), r),
+                    apply<MODE>(bf16_lo(v.w), r), apply<MODE>(bf16_hi(v.w), r));
+  return o;
+}
+
+__device__ __forceinline__ float absmax8(const uint4 v) {
+  // |bf16| as float: clear the sign bits, then widen.
+  const uint32_t m = 0x7FFF7FFFu;
+  const uint32_t a = v.x & m, b = v.y & m, c = v.z & m, d = v.w & m;
+  float r = fmaxf(bf16_lo(a), bf16_hi(a));
+  r = fmaxf(r, fmaxf(bf16_lo(b), bf16_hi(b)));
+  r = fmaxf(r, fmaxf(bf16_lo(c), bf16_hi(c)));
+  r = fmaxf(r, fmaxf(bf16_lo(d), bf16_hi(d)));
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Activations.  A workgroup of 256 lanes covers 16 rows x 4 groups: each
+// 16-lane DPP row owns one activation row and walks 4 consecutive groups, one
+// 16-byte load per lane per group (16 lanes x 16 B = one 128-element group).
+// Blocks are ordered group-block fastest so neighbouring workgroups stream
+// neighbouring kilobytes of the same rows.
+constexpr int kActRows = 16;
+constexpr int kActGroupsPerBlock = 4;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void quantize_act_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, uint8_t* __restrict__ q,
+    float* __restrict__ s, int64_t n_gblk) {
+  const int64_t G = K / kGroup;
+  const int64_t bid = blockIdx.x;
+  const int64_t gb = bid % n_gblk;
+  const int64_t rb = bid / n_gblk;
+  const int unit = threadIdx.x >> 4;
+  const int l16 = threadIdx.x & 15;
+  const int64_t m = rb * kActRows + unit;
+  const bool row_ok = m < M;
+
+  uint4 v[kActGroupsPerBlock];
+#pragma unroll
+  for (int j = 0; j < kActGroupsPerBlock; ++j) {
+    const int64_t g = gb * kActGroupsPerBlock + j;
+    if (row_ok && g < G)
+      v[j] = *reinterpret_cast<const uint4*>(x + m * K + g * kGroup + l16 * 8);
+    else
+      v[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int j = 0; j < kActGroupsPerBlock; ++j) {
+    const int64_t g = gb * kActGroupsPerBlock + j;
+    const float amax = row16_max(absmax8(v[j]));
+    const GroupRule r = group_rule<MODE>(amax);
+    if (row_ok && g < G) {
+      *reinterpret_cast<uint2*>(q + m * K + g * kGroup + l16 * 8) = convert8<MODE>(v[j], r);
+      if (l16 == j) s[g * M + m] = r.s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weights.  One 256-lane workgroup per 128x128 block: lane (r0 = t/16,
+// c = t%16) loads rows r0, r0+16, ..., r0+112 at byte column 16c, so all
+// eight 16-byte loads are in flight before the reduction.  The block max is
+// reduced across each DPP row, across the 4 rows of a wave by readlane, and
+// across the 4 waves through LDS.
+template <int MODE>
+__global__ __launch_bounds__(256) void quantize_weight_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ q,
+    float* __restrict__ s, int64_t KB) {
+  __shared__ float red[4];
+  const int64_t bid = blockIdx.x;
+  const int64_t nb = bid / KB;
+  const int64_t kb = bid % KB;
+  const int t = threadIdx.x;
+  const int l16 = t & 15;
+  const int r0 = t >> 4;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = nb * kGroup + r0 + 16 * i;
+    v[i] = *reinterpret_cast<const uint4*>(w + row * K + kb * kGroup + l16 * 8);
+  }
+  float a = absmax8(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) a = fmaxf(a, absmax8(v[i]));
+  a = row16_max(a);
+  a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16))),
+            fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48))));
+  if (lane == 0) red[wave] = a;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const GroupRule r = group_rule<MODE>(amax);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = nb * kGroup + r0 + 16 * i;
+    *reinterpret_cast<uint2*>(q + row * K + kb * kGroup + l16 * 8) = convert8<MODE>(v[i], r);
+  }
+  if (t == 0) s[nb * KB + kb] = r.s;
+  (void)N;
+}
+
+hipError_t launch_quantize_act(const void* x, int64_t M, int64_t K, uint8_t* q, float* s,
+                               int mode, hipStream_t stream) {
+  const int64_t G = K / kGroup;
+  const int64_t n_gblk = (G + kActGroupsPerBlock - 1) / kActGroupsPerBlock;
+  const int64_t n_rblk = (M + kActRows - 1) / kActRows;
+  const int64_t blocks = n_gblk * n_rblk;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL(quantize_act_kernel<0>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), M, K, q, s, n_gblk);
+  else
+    hipLaunchKernelGGL(quantize_act_kernel<1>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), M, K, q, s, n_gblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const void* w, int64_t N, int64_t K, uint8_t* q, float* s,
+                                  int mode, hipStream_t stream) {
+  const int64_t KB = K / kGroup;
+  const int64_t blocks = (N / kGroup) * KB;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL(quantize_weight_kernel<0>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), N, K, q, s, KB);
+  else
+    hipLaunchKernelGGL(quantize_weight_kernel<1>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), N, K, q, s, KB);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q

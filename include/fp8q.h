@@ -1,0 +1,152 @@
+/*
+ * fp8q.h -- C ABI of the MI355X (gfx950) fine-grained block-scaled FP8 library.
+ *
+ * The method (pages cited by site and passage; they carry no section numbers):
+ *   - the-good.kr free board post 2169793, fine-grained quantization passage:
+ *     the max-abs is computed online for every 1x128 activation tile and every
+ *     128x128 weight block, the scaling factor is derived from it, and the
+ *     values are cast to FP8 online; E4M3 (4-bit exponent, 3-bit mantissa) is
+ *     used for all tensors (mixed-precision framework passage).
+ *   - why-be.co.kr as_center post 57820, promotion passage: once an interval
+ *     of N_C elements along K is reached, the partial results are moved out of
+ *     the matrix unit, multiplied by the scaling factors and added into FP32
+ *     registers; pkd.ac.th webboard post 78017 (increased-precision
+ *     accumulation passage) fixes N_C = 128.
+ *   - why-be.co.kr as_center post 57820 / pkd.ac.th webboard post 78017,
+ *     inference-deployment passages: per-expert GEMMs over small token batches
+ *     (routed top-8 of 256 experts), memory-bound in decoding.
+ *
+ * Conventions for every call:
+ *   - Every data pointer is a DEVICE pointer on the current HIP device.  The
+ *     caller allocates and frees all memory; the library allocates nothing,
+ *     keeps no pointer after returning, creates no stream and never
+ *     synchronizes.  Work is enqueued on `stream` (NULL = the default stream)
+ *     and runs asynchronously.
+ *   - Layouts are packed, row-major, with no stride arguments.
+ *   - Arguments are validated on the host before any device call, in this
+ *     order: NULL pointers (a pointer may be NULL only when its extent is 0),
+ *     shapes, alignment, enums, then the current device must be gfx950.  A
+ *     validation error returns without side effects.  A launch failure
+ *     returns FP8Q_ERR_LAUNCH; output contents are then undefined.
+ *   - Inputs must be finite; outputs must not alias inputs.
+ *   - E4M3 here is the OCP "E4M3FN" encoding (bias 7, no infinities, max 448).
+ *   - Thread-safe; the only global state is a per-device architecture cache.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8Q_ABI_VERSION 1
+
+typedef enum {
+  FP8Q_OK = 0,
+  FP8Q_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  FP8Q_ERR_SHAPE = 2,       /* negative size, or K / N not a multiple of 128,
+                               or G < 1                                          */
+  FP8Q_ERR_ALIGN = 3,       /* data pointer not 16-byte aligned, or scale /
+                               offset pointer not 4-byte aligned                 */
+  FP8Q_ERR_ENUM = 4,        /* unknown scale mode or output dtype              */
+  FP8Q_ERR_DEVICE = 5,      /* no current HIP device, or it is not gfx950      */
+  FP8Q_ERR_LAUNCH = 6,      /* the kernel launch failed                        */
+  FP8Q_ERR_UNSUPPORTED = 7  /* valid request this build does not implement     */
+} fp8q_status;
+
+typedef enum {
+  /* s = fl32(amax / 448); codes = E4M3_RNE(fl32(x * fl32(448 / amax))).
+     A group whose 448/amax is not finite (amax == 0 or below 448/FLT_MAX)
+     is flushed: s = 0 and every code is a signed zero (0x00 / 0x80).      */
+  FP8Q_SCALE_F32 = 0,
+  /* s = 2^e, e the smallest integer with 448 * 2^e >= amax (why-be.co.kr
+     as_center post 72410: scaling factors that are integral powers of 2);
+     codes = E4M3_RNE(x * 2^-e).  amax == 0 gives s = 0 and signed zeros. */
+  FP8Q_SCALE_POW2 = 1
+} fp8q_scale_mode;
+
+typedef enum {
+  FP8Q_OUT_F32 = 0,   /* C stored as float32                              */
+  FP8Q_OUT_BF16 = 1   /* C stored as bfloat16, round-to-nearest-even of
+                         the FP32 accumulator                             */
+} fp8q_out_dtype;
+
+/*
+ * 1x128 activation quantization (fine-grained quantization passage of the
+ * the-good.kr post: one scale per activation row and 128 consecutive K).
+ *   x_bf16 : [M][K] bfloat16, row-major; 16-byte aligned.
+ *   q      : [M][K] uint8 E4M3 codes (output); 16-byte aligned.
+ *   s      : [K/128][M] float32 scales (output), group-major so that the M
+ *            scales of one K group are contiguous; 4-byte aligned.
+ *   M >= 0 (M == 0 is a no-op), K >= 0 with K % 128 == 0.
+ * Results are bit-exact functions of the input (no reduction-order effects).
+ */
+fp8q_status fp8q_quantize_act(const void* x_bf16, int64_t M, int64_t K,
+                              uint8_t* q, float* s, fp8q_scale_mode mode,
+                              hipStream_t stream);
+
+/*
+ * 128x128 weight-block quantization (same passage: one scale per block of
+ * 128 rows of N by 128 columns of K).
+ *   w_bf16 : [N][K] bfloat16, row-major; 16-byte aligned.
+ *   q      : [N][K] uint8 E4M3 codes (output); 16-byte aligned.
+ *   s      : [N/128][K/128] float32 scales, row-major (output).
+ *   N % 128 == 0, K % 128 == 0.  A stack of G experts' weights [G][N][K]
+ *   may be passed as one [G*N][K] matrix: blocks never straddle experts, and
+ *   the scales come out as [G][N/128][K/128].
+ */
+fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K,
+                                 uint8_t* q, float* s, fp8q_scale_mode mode,
+                                 hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM with promotion every 128 K (promotion passage of the
+ * why-be.co.kr post 57820, interval from the pkd.ac.th post):
+ *   C[m][n] = sum_g (a_s[g][m] * w_s[n/128][g]) * P_g[m][n],
+ *   P_g[m][n] = sum_{k in [128g, 128g+128)} dec(a_q[m][k]) * dec(w_q[n][k]);
+ * each P_g is formed by the matrix cores from a zero start and folded into
+ * the FP32 accumulator by a fused multiply-add on the vector ALUs.
+ *   a_q : [M][K] uint8, a_s : [K/128][M] float32  (from fp8q_quantize_act)
+ *   w_q : [N][K] uint8, w_s : [N/128][K/128] float32 (from fp8q_quantize_weight)
+ *   c   : [M][N] float32 or bfloat16 (per `out`), row-major (output).
+ *   M >= 0, N % 128 == 0, K % 128 == 0.
+ * Accuracy: |C - C_exact| <= 1e-5 * sum_k |dec(a)*s_a| * |dec(w)*s_w| per
+ * element (plus half a BF16 ulp for BF16 output).
+ */
+fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s,
+                      const uint8_t* w_q, const float* w_s,
+                      int64_t M, int64_t N, int64_t K,
+                      void* c, fp8q_out_dtype out, hipStream_t stream);
+
+/*
+ * Grouped (per-expert) variant.  Rows [off[e], off[e+1]) of a_q use expert
+ * e's weights w_q + e*N*K and scales w_s + e*(N/128)*(K/128).
+ *   a_q : [M_total][K] uint8, a_s : [K/128][M_total] float32.
+ *   off : DEVICE int32[G+1] with 0 = off[0] <= off[1] <= ... <= off[G] <=
+ *         M_total (unchecked on the device: a violation gives undefined
+ *         output); experts with no rows are allowed.
+ *   w_q : [G][N][K] uint8, w_s : [G][N/128][K/128] float32.
+ *   c   : [M_total][N] (output); rows >= off[G] are left untouched.
+ *   G >= 1, N % 128 == 0, K % 128 == 0.  No host synchronization is needed
+ *   between the producer of `off` and this call.
+ */
+fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                              const int32_t* off, int32_t G,
+                              const uint8_t* w_q, const float* w_s,
+                              int64_t N, int64_t K,
+                              void* c, fp8q_out_dtype out, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fp8q_status_string(fp8q_status status);
+
+/* FP8Q_ABI_VERSION of the loaded library. */
+int fp8q_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

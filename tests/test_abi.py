@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp8q.h declares, and rejects invalid arguments on the host with the
+documented status codes before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+LIB = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "libfp8q.so")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_DEVICE, E_LAUNCH, E_UNSUP = range(8)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8q_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfp8q.so is not built (python -m fine_grained_block_fp8q_amd.build)")
+    L = ctypes.CDLL(LIB)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.fp8q_quantize_act.argtypes = [p, i64, i64, p, p, i32, p]
+    L.fp8q_quantize_weight.argtypes = [p, i64, i64, p, p, i32, p]
+    L.fp8q_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
+    L.fp8q_grouped_gemm.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
+    L.fp8q_status_string.restype = ctypes.c_char_p
+    L.fp8q_status_string.argtypes = [ctypes.c_int]
+    return L
+
+
+def _no_device():
+    """True when no GPU is visible (the fake pointers below must never reach a
+    kernel).  device_count() does not initialise the GPU."""
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) >= {"fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm",
+                          "fp8q_grouped_gemm", "fp8q_status_string", "fp8q_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fp8q_abi_version() == 1
+    for s in range(8):
+        txt = lib.fp8q_status_string(s).decode()
+        assert txt.startswith("FP8Q_")
+    assert "UNKNOWN" in lib.fp8q_status_string(99).decode()
+
+
+A = 0x10000  # fake, 64 KiB-aligned "device" addresses: never dereferenced on these paths
+
+
+def test_quantize_act_validation(lib):
+    f = lib.fp8q_quantize_act
+    assert f(None, 4, 128, A, A, 0, None) == E_NULL
+    assert f(A, 4, 128, None, A, 0, None) == E_NULL
+    assert f(A, 4, 128, A, None, 0, None) == E_NULL
+    assert f(None, 0, 128, None, None, 0, None) == OK  # empty is a no-op
+    assert f(A, -1, 128, A, A, 0, None) == E_SHAPE
+    assert f(A, 4, 100, A, A, 0, None) == E_SHAPE
+    assert f(A, 4, -128, A, A, 0, None) == E_SHAPE
+    assert f(A + 8, 4, 128, A, A, 0, None) == E_ALIGN
+    assert f(A, 4, 128, A + 4, A, 0, None) == E_ALIGN
+    assert f(A, 4, 128, A, A + 2, 0, None) == E_ALIGN
+    assert f(A, 4, 128, A, A, 2, None) == E_ENUM
+    assert f(A, 4, 128, A, A, -1, None) == E_ENUM
+
+
+def test_quantize_weight_validation(lib):
+    f = lib.fp8q_quantize_weight
+    assert f(None, 128, 128, A, A, 0, None) == E_NULL
+    assert f(A, 100, 128, A, A, 0, None) == E_SHAPE
+    assert f(A, 128, 130, A, A, 0, None) == E_SHAPE
+    assert f(A + 16 + 8, 128, 128, A, A, 0, None) == E_ALIGN
+    assert f(A, 128, 128, A, A, 7, None) == E_ENUM
+    assert f(None, 0, 0, None, None, 0, None) == OK
+
+
+def test_gemm_validation(lib):
+    f = lib.fp8q_gemm
+    assert f(A, A, A, A, 4, 128, 128, None, 0, None) == E_NULL
+    assert f(None, A, A, A, 4, 128, 128, A, 0, None) == E_NULL
+    assert f(A, None, A, A, 4, 128, 128, A, 0, None) == E_NULL
+    assert f(A, A, A, A, 4, 100, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, A, A, 4, 128, 64, A, 0, None) == E_SHAPE
+    assert f(A, A, A, A, -4, 128, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, A + 1, A, 4, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A + 1, A, A, 4, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A, A, A, 4, 128, 128, A + 8, 0, None) == E_ALIGN
+    assert f(A, A, A, A, 4, 128, 128, A, 3, None) == E_ENUM
+    assert f(None, None, None, None, 0, 128, 128, None, 0, None) == OK
+
+
+def test_grouped_gemm_validation(lib):
+    f = lib.fp8q_grouped_gemm
+    assert f(A, A, 8, None, 2, A, A, 128, 128, A, 0, None) == E_NULL
+    assert f(A, A, 8, A, 2, A, A, 128, 128, None, 0, None) == E_NULL
+    assert f(A, A, 8, A, 0, A, A, 128, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, 8, A, 2, A, A, 200, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, -8, A, 2, A, A, 128, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, 8, A + 2, 2, A, A, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A, 8, A, 2, A, A, 128, 128, A, 5, None) == E_ENUM
+    assert f(A, A, 8, A, 2000, A, A, 128, 128, A, 0, None) == E_UNSUP
+    assert f(None, None, 0, A, 2, None, None, 128, 128, None, 0, None) == OK
+
+
+def test_valid_arguments_without_gpu_report_device_error(lib):
+    if not _no_device():
+        pytest.skip("a GPU is visible: fake pointers must not be launched")
+    assert lib.fp8q_quantize_act(A, 4, 128, A, A, 0, None) == E_DEVICE
+    assert lib.fp8q_quantize_weight(A, 128, 128, A, A, 1, None) == E_DEVICE
+    assert lib.fp8q_gemm(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
+    assert lib.fp8q_grouped_gemm(A, A, 8, A, 2, A, A, 128, 128, A, 0, None) == E_DEVICE
