@@ -30,7 +30,9 @@ COMMON = [
 # no FP contraction and no fast math there.
 SOURCES = {
     "quant_kernels.hip": ["-ffp-contract=off"],
-    "gemm_kernels.hip": [],
+    # keep MFMA results in arch VGPRs: the promotion FMAs read them directly
+    # instead of copying each element out of an AGPR first
+    "gemm_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "fp8q_api.hip": [],
 }
 

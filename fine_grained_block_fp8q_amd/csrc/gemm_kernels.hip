@@ -10,134 +10,189 @@
 // MI355X mapping.  One v_mfma_f32_16x16x128_f8f6f4 consumes exactly one
 // 128-wide K chunk of a 16x16 output block, so each chunk's partial P_g is a
 // single MFMA started from zero; the promotion acc = fma(P_g, s_a*s_w, acc) is
-// four VALU FMAs per MFMA.  Two waves share each SIMD, so one wave's FMAs
-// overlap the other wave's MFMAs (the role the pages give to two alternating
-// warpgroups on Hopper).
+// four VALU FMAs per MFMA.  Inside a wave the column blocks are software
+// pipelined: the MFMAs of block j run on the matrix core while the VALU folds
+// block j-1's partials into the accumulators (the role the pages give to two
+// alternating warpgroups on Hopper).
 //
-// Workgroup tile BM x BN with 8 waves (4 along M x 2 along N), wave tile
-// 64 x 128: each wave's 128 columns are one weight block, so s_w is a single
-// wave-uniform scalar per chunk.  Operands move HBM/L2 -> LDS with 16-byte
-// direct-to-LDS loads (no VGPR staging), double-buffered over K chunks with
-// one barrier per chunk.  LDS rows are 128 bytes (one chunk of K) with the
-// 16-byte column index XOR-swizzled by (row & 7) so MFMA fragment reads are
-// bank-conflict free.
+// Each wave owns a 64 x 128 output tile: its 128 columns are one weight
+// block, so s_w is one wave-uniform scalar per chunk, and its 64 row scales are
+// one 256-byte LDS slot per chunk.  Operands move HBM/L2 -> LDS with 16-byte
+// direct-to-LDS loads (no VGPR staging) through a ring of STAGES K chunks, one
+// barrier per chunk.  LDS rows are 128 bytes (one K chunk) with the 16-byte
+// column index XOR-swizzled per row so fragment reads are bank-conflict free.
 
 #include "fp8q_device.hpp"
 
 namespace fp8q {
 
-namespace gemm_cfg {
-constexpr int BM = 256;
-constexpr int BN = 256;
-constexpr int BK = 128;                       // one promotion interval
-constexpr int WAVES_M = 4;
-constexpr int WAVES_N = 2;
-constexpr int NWAVES = WAVES_M * WAVES_N;     // 8
-constexpr int THREADS = NWAVES * 64;          // 512
-constexpr int WM = BM / WAVES_M;              // 64
-constexpr int WN = BN / WAVES_N;              // 128 = one weight block
-constexpr int MB = WM / 16;                   // 4 MFMA row blocks per wave
-constexpr int NB = WN / 16;                   // 8 MFMA column blocks per wave
-constexpr int A_BYTES = BM * BK;              // 32 KiB
-constexpr int B_BYTES = BN * BK;              // 32 KiB
-constexpr int SA_BYTES = BM * 4;              // 1 KiB
-constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
-constexpr int STAGES = 2;
-constexpr int LDS_BYTES = STAGE * STAGES;     // 130 KiB of the 160 KiB
-static_assert(WN == 128, "a wave's columns must be one 128-wide weight block");
-}  // namespace gemm_cfg
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct GemmCfg {
+  static constexpr int BM = BM_;
+  static constexpr int BN = BN_;
+  static constexpr int BK = 128;                    // one promotion interval
+  static constexpr int WAVES_M = WAVES_M_;
+  static constexpr int WAVES_N = WAVES_N_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = NWAVES * 64;
+  static constexpr int WM = BM / WAVES_M;
+  static constexpr int WN = BN / WAVES_N;
+  static constexpr int MB = WM / 16;                // MFMA row blocks per wave
+  static constexpr int NB = WN / 16;                // MFMA column blocks per wave
+  static constexpr int A_BYTES = BM * BK;
+  static constexpr int B_BYTES = BN * BK;
+  static constexpr int SA_BYTES = NWAVES * 256;     // 64 row scales per wave
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int LDS_BYTES = STAGE * STAGES;
+  static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;   // per wave per chunk
+  static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
+  static constexpr int LOADS = A_INSTR + B_INSTR + 1;        // + the scale slot
+  static_assert(WM == 64, "a wave's rows are 64 (one 256-byte scale slot)");
+  static_assert(WN == 128, "a wave's columns must be one 128-wide weight block");
+  static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0,
+                "tile loads must split evenly over the waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && STAGES <= 4 && LOADS * (STAGES - 2) < 64, "vmcnt range");
+};
+
+// Dense configuration: 256 x 256 tiles, 8 waves (two per SIMD, so one wave's
+// promotion FMAs overlap the other's MFMAs), 2 stages (130 KiB of LDS).
+using DenseCfg = GemmCfg<256, 256, 4, 2, 2>;
+// Grouped configuration: 256-row tiles cover an expert's tokens (decode
+// batches hold at most 256) so each expert's weights stream once per n-tile.
+using GroupedCfg = GemmCfg<256, 128, 4, 1, 3>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ lds_ptr_t to_lds(uint8_t* p) {
-  return (lds_ptr_t)(p);
+__device__ __forceinline__ lds_ptr_t to_lds(uint8_t* p) { return (lds_ptr_t)(p); }
+
+// Physical 16-byte column of logical column c in LDS row r.  A fragment read
+// has 16 lanes on 16 consecutive 128-byte rows at one logical column.  With
+// f(r) = (r/2 mod 8) ^ 4*(r&1), the 8 even rows and the 8 odd rows each take
+// all 8 columns, so the 16 lanes hit 16 distinct 16-byte slots of a 256-byte
+// bank window, and each 8-row half also takes 8 distinct columns: the
+// ds_read_b128 is bank-conflict free with 32 or 64 four-byte banks.  XOR with
+// a per-row constant is an involution, so the same map locates and fetches.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
+
+// s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their maxima (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Physical 16-byte column of logical column c in LDS row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
+// Workgroup barrier that orders LDS accesses but does not drain global loads
+// still in flight (those are waited for explicitly with vmcnt).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-// Issue the direct-to-LDS loads of one K chunk (A tile, W tile, A scales).
+// Wait until at most `after` chunks' loads (issued after the one needed) are
+// still outstanding for this wave.
+template <int LOADS, int MAXA>
+__device__ __forceinline__ void wait_chunk(int after) {
+  if (MAXA >= 2 && after >= 2) wait_vmcnt<LOADS * 2>();
+  else if (MAXA >= 1 && after >= 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+}
+
+// Issue the direct-to-LDS loads of one K chunk (A tile, W tile, row scales).
 // Each load instruction moves 64 lanes x 16 B = 8 LDS rows of 128 B; lane i
 // of the instruction lands at LDS byte 16*i, i.e. row i/8, physical column
 // i%8, and therefore fetches logical column swz(row, i%8) from global memory.
-// Rows past the matrix edge are clamped to the last row (their results are
-// never stored).
+// Rows past the valid range are clamped to the last valid row (their results
+// are never stored).  Every wave issues exactly Cfg::LOADS instructions.
+template <class Cfg>
 __device__ __forceinline__ void issue_chunk(uint8_t* stage, const uint8_t* __restrict__ A,
                                             const float* __restrict__ SA,
                                             const uint8_t* __restrict__ W, int64_t a_row0,
                                             int64_t a_rows, int64_t w_row0, int64_t w_rows,
                                             int64_t K, int64_t sa_ld, int64_t g, int wave,
-                                            int lane) {
-  using namespace gemm_cfg;
+                                            int wave_m, int lane) {
   const int sub_r = lane >> 3;
   const int pc = lane & 7;
-  constexpr int A_INSTR = A_BYTES / 1024;  // 32
-  constexpr int B_INSTR = B_BYTES / 1024;  // 32
 #pragma unroll
-  for (int j = 0; j < A_INSTR / NWAVES; ++j) {
-    const int blk = wave * (A_INSTR / NWAVES) + j;
+  for (int j = 0; j < Cfg::A_INSTR; ++j) {
+    const int blk = wave * Cfg::A_INSTR + j;
     const int r = blk * 8 + sub_r;
     int64_t gr = a_row0 + r;
     gr = gr < a_rows ? gr : a_rows - 1;
-    const uint8_t* src = A + gr * K + g * BK + swz(r, pc) * 16;
+    const uint8_t* src = A + gr * K + g * Cfg::BK + swz(r, pc) * 16;
     __builtin_amdgcn_global_load_lds(src, to_lds(stage + blk * 1024), 16, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < B_INSTR / NWAVES; ++j) {
-    const int blk = wave * (B_INSTR / NWAVES) + j;
+  for (int j = 0; j < Cfg::B_INSTR; ++j) {
+    const int blk = wave * Cfg::B_INSTR + j;
     const int r = blk * 8 + sub_r;
     int64_t gr = w_row0 + r;
     gr = gr < w_rows ? gr : w_rows - 1;
-    const uint8_t* src = W + gr * K + g * BK + swz(r, pc) * 16;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + A_BYTES + blk * 1024), 16, 0, 0);
+    const uint8_t* src = W + gr * K + g * Cfg::BK + swz(r, pc) * 16;
+    __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + blk * 1024), 16, 0, 0);
   }
-  // A scales of this chunk: BM floats, 64 per dword-load instruction.
-  if (wave < BM / 64) {
-    const int r = wave * 64 + lane;
-    int64_t gr = a_row0 + r;
+  {  // this wave's 64 row scales
+    int64_t gr = a_row0 + wave_m * 64 + lane;
     gr = gr < a_rows ? gr : a_rows - 1;
     const float* src = SA + g * sa_ld + gr;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + A_BYTES + B_BYTES + wave * 256), 4, 0,
-                                     0);
+    __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256),
+                                     4, 0, 0);
   }
 }
 
+// MFMA operand fragment: LDS row r, the 32-byte slice q of its 128-byte K
+// chunk (two swizzled 16-byte columns).  A and B fragments use the same
+// (q, byte) -> K mapping, so every product pairs matching K indices.
+__device__ __forceinline__ v8i load_frag(const uint8_t* base, int r, int q) {
+  const v4i lo = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, 2 * q) * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, 2 * q + 1) * 16);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Promotion of one 16x16 chunk partial: acc += P * (s_a[row] * s_w).
+__device__ __forceinline__ void promote(v4f& acc, const v4f& p, const v4f& mult) {
+  acc[0] = __builtin_fmaf(p[0], mult[0], acc[0]);
+  acc[1] = __builtin_fmaf(p[1], mult[1], acc[1]);
+  acc[2] = __builtin_fmaf(p[2], mult[2], acc[2]);
+  acc[3] = __builtin_fmaf(p[3], mult[3], acc[3]);
+}
+
 struct TileArgs {
-  const uint8_t* A;     // [a_rows][K] rows of this problem
+  const uint8_t* A;     // rows of A (absolute row index)
   const float* SA;      // SA[g * sa_ld + row]
   const uint8_t* W;     // [w_rows][K]
   const float* SW;      // [w_rows/128][K/128]
   int64_t a_row0;       // first A row of the tile
-  int64_t a_rows;       // rows of A valid for this tile (exclusive end, absolute)
+  int64_t a_rows;       // exclusive end of the valid A rows
   int64_t w_row0;       // first W row (= output column) of the tile
   int64_t w_rows;       // N
   int64_t K;
-  int64_t sa_ld;        // leading dimension of SA (M_total)
+  int64_t sa_ld;        // leading dimension of SA (total rows)
   void* C;              // output base
   int64_t ldc;          // N
   int out_bf16;
 };
 
-// Computes one BM x BN output tile.  All 512 lanes of the workgroup call it.
+// Computes one BM x BN output tile.  All lanes of the workgroup call it.
+template <class Cfg>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
-  using namespace gemm_cfg;
+  constexpr int MB = Cfg::MB, NB = Cfg::NB, S = Cfg::STAGES;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave_m = wave / WAVES_N;
-  const int wave_n = wave % WAVES_N;
+  const int wave_m = wave / Cfg::WAVES_N;
+  const int wave_n = wave % Cfg::WAVES_N;
   const int r16 = lane & 15;   // fragment row (A) / column (B) within a 16-block
   const int q = lane >> 4;     // which 32-byte slice of the 128-byte chunk
-  const int64_t G = t.K / BK;
-  const int64_t KB = G;
+  const int64_t G = t.K / Cfg::BK;
 
-  // Output column block of this wave and its weight-scale row.
-  int64_t wblk = (t.w_row0 + wave_n * WN) / 128;
+  // Weight-scale row of this wave's 128 columns.
+  int64_t wblk = (t.w_row0 + wave_n * Cfg::WN) / 128;
   const int64_t last_wblk = t.w_rows / 128 - 1;
   wblk = wblk < last_wblk ? wblk : last_wblk;
-  const float* sw_row = t.SW + wblk * KB;
+  const float* sw_row = t.SW + wblk * G;
 
   // Waves whose rows are all past the valid range skip the MFMA work.
-  const bool wave_live = (t.a_row0 + wave_m * WM) < t.a_rows;
+  const bool wave_live = (t.a_row0 + wave_m * Cfg::WM) < t.a_rows;
 
   v4f acc[MB][NB];
 #pragma unroll
@@ -145,49 +200,68 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  issue_chunk(smem, t.A, t.SA, t.W, t.a_row0, t.a_rows, t.w_row0, t.w_rows, t.K, t.sa_ld, 0,
-              wave, lane);
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < G)
+      issue_chunk<Cfg>(smem + s * Cfg::STAGE, t.A, t.SA, t.W, t.a_row0, t.a_rows, t.w_row0,
+                       t.w_rows, t.K, t.sa_ld, s, wave, wave_m, lane);
 
+  int cur_stage = 0;
   for (int64_t g = 0; g < G; ++g) {
-    uint8_t* cur = smem + (g & 1) * STAGE;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's chunk-g loads landed
-    __syncthreads();                     // every wave's loads landed; stage g+1 free
-    if (g + 1 < G)
-      issue_chunk(smem + ((g + 1) & 1) * STAGE, t.A, t.SA, t.W, t.a_row0, t.a_rows, t.w_row0,
-                  t.w_rows, t.K, t.sa_ld, g + 1, wave, lane);
+    // This wave's loads of chunk g have landed once at most the chunks issued
+    // after it (up to S-2 of them) are still outstanding.
+    {
+      const int64_t left = G - 1 - g;
+      wait_chunk<Cfg::LOADS, S - 2>(left < S - 2 ? (int)left : S - 2);
+    }
+    lds_barrier();  // every wave's chunk g landed; chunk g-1's stage is free
+    {
+      const int64_t gn = g + S - 1;
+      if (gn < G) {
+        int st = cur_stage + S - 1;
+        st = st >= S ? st - S : st;
+        issue_chunk<Cfg>(smem + st * Cfg::STAGE, t.A, t.SA, t.W, t.a_row0, t.a_rows, t.w_row0,
+                         t.w_rows, t.K, t.sa_ld, gn, wave, wave_m, lane);
+      }
+    }
+    const uint8_t* As = smem + cur_stage * Cfg::STAGE;
+    const uint8_t* Bs = As + Cfg::A_BYTES;
+    const float* SAs = reinterpret_cast<const float*>(As + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256);
+    cur_stage = cur_stage + 1 == S ? 0 : cur_stage + 1;
     if (!wave_live) continue;
 
-    const uint8_t* As = cur;
-    const uint8_t* Bs = cur + A_BYTES;
-    const float* SAs = reinterpret_cast<const float*>(cur + A_BYTES + B_BYTES);
     const float sw = sw_row[g];
-
     v8i a[MB];
     v4f mult[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int r = wave_m * WM + i * 16 + r16;
-      const v4i lo = *reinterpret_cast<const v4i*>(As + r * BK + swz(r, 2 * q) * 16);
-      const v4i hi = *reinterpret_cast<const v4i*>(As + r * BK + swz(r, 2 * q + 1) * 16);
-      a[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const v4f sa = *reinterpret_cast<const v4f*>(SAs + wave_m * WM + i * 16 + 4 * q);
+      a[i] = load_frag(As, wave_m * Cfg::WM + i * 16 + r16, q);
+      const v4f sa = *reinterpret_cast<const v4f*>(SAs + i * 16 + 4 * q);
       mult[i] = sa * sw;
     }
+    // Software pipeline over the MB x NB blocks (row block fastest, so one B
+    // fragment serves MB MFMAs): the MFMA of block k+1 is issued before the
+    // VALU folds block k's partial, so the matrix core and the VALU overlap
+    // with only two partials live; block j+1's B fragment is read from LDS
+    // while block j's MFMAs run.
+    v8i b[2];
+    v4f p[2];
+    b[0] = load_frag(Bs, wave_n * Cfg::WN + r16, q);
+    p[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], b[0], v4f{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int r = wave_n * WN + j * 16 + r16;
-      const v4i lo = *reinterpret_cast<const v4i*>(Bs + r * BK + swz(r, 2 * q) * 16);
-      const v4i hi = *reinterpret_cast<const v4i*>(Bs + r * BK + swz(r, 2 * q + 1) * 16);
-      const v8i b = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a[i], b, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        acc[i][j][0] = __builtin_fmaf(p[0], mult[i][0], acc[i][j][0]);
-        acc[i][j][1] = __builtin_fmaf(p[1], mult[i][1], acc[i][j][1]);
-        acc[i][j][2] = __builtin_fmaf(p[2], mult[i][2], acc[i][j][2]);
-        acc[i][j][3] = __builtin_fmaf(p[3], mult[i][3], acc[i][j][3]);
-      }
+    for (int k = 1; k < MB * NB; ++k) {
+      const int i = k % MB, j = k / MB;
+      if (i == 1 && j + 1 < NB)
+        b[(j + 1) & 1] = load_frag(Bs, wave_n * Cfg::WN + (j + 1) * 16 + r16, q);
+      p[k & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          a[i], b[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      const int kp = k - 1;
+      promote(acc[kp % MB][kp / MB], p[kp & 1], mult[kp % MB]);
+    }
+    {
+      const int kp = MB * NB - 1;
+      promote(acc[kp % MB][kp / MB], p[kp & 1], mult[kp % MB]);
     }
   }
 
@@ -197,11 +271,11 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   for (int i = 0; i < MB; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t row = t.a_row0 + wave_m * WM + i * 16 + 4 * q + v;
+      const int64_t row = t.a_row0 + wave_m * Cfg::WM + i * 16 + 4 * q + v;
       if (row >= t.a_rows) continue;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int64_t col = t.w_row0 + wave_n * WN + j * 16 + r16;
+        const int64_t col = t.w_row0 + wave_n * Cfg::WN + j * 16 + r16;
         if (col >= t.w_rows) continue;
         if (t.out_bf16)
           reinterpret_cast<uint16_t*>(t.C)[row * t.ldc + col] =
@@ -213,30 +287,50 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   }
 }
 
-__global__ __launch_bounds__(gemm_cfg::THREADS) void gemm_kernel(
+// Workgroup id -> output tile.  Workgroups are dispatched round-robin over
+// the 8 XCDs (id mod 8), each with its own L2.  Give each XCD a contiguous
+// run of tile ids, and walk tiles in groups of kGroupM tile rows (tile row
+// fastest), so an XCD's tiles form a compact kGroupM x (run / kGroupM) block
+// that shares A row bands and W column bands in that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tiles_n, int& tm, int& tn) {
+  int id = bid;
+  if (nblocks % kXcds == 0) id = (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+  const int tiles_m = nblocks / tiles_n;
+  const int per_group = kGroupM * tiles_n;
+  const int grp = id / per_group;
+  const int first_m = grp * kGroupM;
+  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int in = id - grp * per_group;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, const uint8_t* __restrict__ W,
     const float* __restrict__ SW, int64_t M, int64_t N, int64_t K, void* __restrict__ C,
     int out_bf16, int tiles_n) {
-  using namespace gemm_cfg;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
-  const int tile = blockIdx.x;
-  const int tm = tile / tiles_n;
-  const int tn = tile % tiles_n;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS_BYTES];
+  int tm, tn;
+  xcd_tile(blockIdx.x, gridDim.x, tiles_n, tm, tn);
   TileArgs t;
   t.A = A;
   t.SA = SA;
   t.W = W;
   t.SW = SW;
-  t.a_row0 = (int64_t)tm * BM;
+  t.a_row0 = (int64_t)tm * Cfg::BM;
   t.a_rows = M;
-  t.w_row0 = (int64_t)tn * BN;
+  t.w_row0 = (int64_t)tn * Cfg::BN;
   t.w_rows = N;
   t.K = K;
   t.sa_ld = M;
   t.C = C;
   t.ldc = N;
   t.out_bf16 = out_bf16;
-  gemm_tile(t, smem);
+  gemm_tile<Cfg>(t, smem);
 }
 
 // Grouped variant.  The grid over-provisions tiles; each workgroup maps its id
@@ -244,39 +338,40 @@ __global__ __launch_bounds__(gemm_cfg::THREADS) void gemm_kernel(
 // offsets, held in LDS.  Workgroups past the last tile exit.
 constexpr int kMaxExpertsLds = 1024;
 
-__global__ __launch_bounds__(gemm_cfg::THREADS) void grouped_gemm_kernel(
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, int64_t M_total,
     const int32_t* __restrict__ off, int G, const uint8_t* __restrict__ W,
     const float* __restrict__ SW, int64_t N, int64_t K, void* __restrict__ C, int out_bf16,
     int tiles_n) {
-  using namespace gemm_cfg;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  constexpr int T = Cfg::THREADS;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS_BYTES];
+  static_assert((kMaxExpertsLds + 1 + T) * 4 <= Cfg::LDS_BYTES, "prefix scratch fits in LDS");
   int* mt_prefix = reinterpret_cast<int*>(smem);  // [G + 1], reused before the mainloop
+  int* scan = mt_prefix + kMaxExpertsLds + 1;     // [T]
 
-  // Prefix over experts of the number of BM-row tiles (serial chunks of
-  // THREADS experts with a block scan each).
+  // Prefix over experts of the number of BM-row tiles (chunks of T experts,
+  // each with a Hillis-Steele block scan).
   const int tid = threadIdx.x;
   int running = 0;
   if (tid == 0) mt_prefix[0] = 0;
-  for (int base = 0; base < G; base += THREADS) {
+  for (int base = 0; base < G; base += T) {
     const int e = base + tid;
     int cnt = 0;
     if (e < G) {
       const int rows = off[e + 1] - off[e];
-      cnt = rows > 0 ? (rows + BM - 1) / BM : 0;
+      cnt = rows > 0 ? (rows + Cfg::BM - 1) / Cfg::BM : 0;
     }
-    // inclusive scan across the workgroup through LDS (Hillis-Steele)
-    int* scan = mt_prefix + kMaxExpertsLds + 1;
     scan[tid] = cnt;
     __syncthreads();
-    for (int d = 1; d < THREADS; d <<= 1) {
+    for (int d = 1; d < T; d <<= 1) {
       const int add = tid >= d ? scan[tid - d] : 0;
       __syncthreads();
       scan[tid] += add;
       __syncthreads();
     }
     if (e < G) mt_prefix[e + 1] = running + scan[tid];
-    running += scan[THREADS - 1];
+    running += scan[T - 1];
     __syncthreads();
   }
   const int total_mtiles = running;
@@ -284,7 +379,7 @@ __global__ __launch_bounds__(gemm_cfg::THREADS) void grouped_gemm_kernel(
   const int mt_global = tile / tiles_n;
   const int tn = tile % tiles_n;
   if (mt_global >= total_mtiles) return;
-  // binary search: expert e with prefix[e] <= mt_global < prefix[e+1]
+  // expert e with prefix[e] <= mt_global < prefix[e+1]
   int lo = 0, hi = G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -301,29 +396,29 @@ __global__ __launch_bounds__(gemm_cfg::THREADS) void grouped_gemm_kernel(
   t.SA = SA;
   t.W = W + (int64_t)e * N * K;
   t.SW = SW + (int64_t)e * (N / 128) * (K / 128);
-  t.a_row0 = r0 + (int64_t)mt * BM;
+  t.a_row0 = r0 + (int64_t)mt * Cfg::BM;
   t.a_rows = r1;
-  t.w_row0 = (int64_t)tn * BN;
+  t.w_row0 = (int64_t)tn * Cfg::BN;
   t.w_rows = N;
   t.K = K;
   t.sa_ld = M_total;
   t.C = C;
   t.ldc = N;
   t.out_bf16 = out_bf16;
-  gemm_tile(t, smem);
+  gemm_tile<Cfg>(t, smem);
 }
 
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
                        const float* w_s, int64_t M, int64_t N, int64_t K, void* c, int out_bf16,
                        hipStream_t stream) {
-  using namespace gemm_cfg;
+  using Cfg = DenseCfg;
   if (M == 0 || N == 0) return hipSuccess;
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+  const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)tiles), dim3(THREADS), 0, stream, a_q, a_s, w_q,
-                     w_s, M, N, K, c, out_bf16, (int)tiles_n);
+  hipLaunchKernelGGL(gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream, a_q,
+                     a_s, w_q, w_s, M, N, K, c, out_bf16, (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -331,16 +426,17 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
                                const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
                                int64_t N, int64_t K, void* c, int out_bf16,
                                hipStream_t stream) {
-  using namespace gemm_cfg;
+  using Cfg = GroupedCfg;
   if (M_total == 0 || N == 0) return hipSuccess;
   if (G > kMaxExpertsLds) return hipErrorInvalidValue;
-  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
   // sum_e ceil(M_e / BM) <= floor(M_total / BM) + G
-  const int64_t max_mtiles = M_total / BM + G;
+  const int64_t max_mtiles = M_total / Cfg::BM + G;
   const int64_t tiles = max_mtiles * tiles_n;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)tiles), dim3(THREADS), 0, stream, a_q,
-                     a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16, (int)tiles_n);
+  hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0,
+                     stream, a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16,
+                     (int)tiles_n);
   return hipGetLastError();
 }
 
