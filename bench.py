@@ -46,7 +46,22 @@ def parse():
     p.add_argument("--workload", default="dense", choices=["dense", "moe", "decode", "largek"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (3 times): the known-size "
+                        "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 3}))
 
 
 def gemm_bytes(M, N, K, out_bytes):
@@ -74,15 +89,20 @@ def setup_dense(fq, torch, name, sets):
         C = torch.empty((M, N), dtype=torch.float32, device=dev)
         bufs.append((A, W, aq, as_, wq, ws, C))
 
-    def step(i, ev):
+    def launch(name, i):
         A, W, aq, as_, wq, ws, C = bufs[i % sets]
-        ev[0].record()
-        fq.fp8q_quantize_act(A, aq, as_)
-        ev[1].record()
-        fq.fp8q_quantize_weight(W, wq, ws)
-        ev[2].record()
-        fq.fp8q_gemm(aq, as_, wq, ws, C)
-        ev[3].record()
+        if name == "fp8q_quantize_act":
+            fq.fp8q_quantize_act(A, aq, as_)
+        elif name == "fp8q_quantize_weight":
+            fq.fp8q_quantize_weight(W, wq, ws)
+        else:
+            fq.fp8q_gemm(aq, as_, wq, ws, C)
+
+    order = ["fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm"]
+
+    def step(i):
+        for name in order:
+            launch(name, i)
 
     kernels = [
         ("fp8q_quantize_act", "hbm", M * K * ACT_BYTES_PER_ELEM, "B"),
@@ -93,7 +113,7 @@ def setup_dense(fq, torch, name, sets):
     cfg = {"workload": f"{name}: A {M}x{K} bf16 (1x128 act quant), W {N}x{K} bf16 "
                        f"(128x128 block quant), C = A W^T fp32",
            "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
-    return step, kernels, flops, cfg, 2 + 1 + 1, (M, N, K)
+    return step, launch, kernels, flops, cfg
 
 
 def setup_grouped(fq, torch, name, sets):
@@ -135,14 +155,16 @@ def setup_grouped(fq, torch, name, sets):
         C = torch.empty((Mt, N), dtype=out_dtype, device=dev)
         bufs.append((A, aq, as_, C))
 
-    def step(i, ev):
+    def launch(name, i):
         A, aq, as_, C = bufs[i % sets]
-        ev[0].record()
-        fq.fp8q_quantize_act(A, aq, as_)
-        ev[1].record()
-        ev[2].record()
-        fq.fp8q_grouped_gemm(aq, as_, d_off, wq, ws, C)
-        ev[3].record()
+        if name == "fp8q_quantize_act":
+            fq.fp8q_quantize_act(A, aq, as_)
+        else:
+            fq.fp8q_grouped_gemm(aq, as_, d_off, wq, ws, C)
+
+    def step(i):
+        launch("fp8q_quantize_act", i)
+        launch("fp8q_grouped_gemm", i)
 
     ob = 2 if out_dtype == torch.bfloat16 else 4
     flops = 2.0 * Mt * N * K
@@ -150,38 +172,69 @@ def setup_grouped(fq, torch, name, sets):
     kernels = [
         ("fp8q_quantize_act", "hbm", Mt * K * ACT_BYTES_PER_ELEM, "B"),
         ("fp8q_grouped_gemm", "hbm", gbytes, "B"),
-        ("fp8q_grouped_gemm:flops", "mfma", flops, "flop"),
     ]
     cfg = {"workload": f"{name}: {G} experts, rows {Mt} (M_e {int(counts.min())}..{int(counts.max())}), "
                        f"N {N}, K {K}, 1x128 act quant + grouped GEMM, weights pre-quantized 128x128",
            "experts": G, "rows": Mt, "N": N, "K": K, "out": "bf16" if ob == 2 else "f32",
            "input_sets": sets}
-    return step, kernels, flops, cfg, None, (Mt, N, K)
+    return step, launch, kernels, flops, cfg
+
+
+# -------------------------------------------------------- recorded traffic
+def kernel_source_digest():
+    """sha256 of the GEMM kernel source: traffic figures recorded under
+    profiles/ are reported only while the kernel is unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "csrc", "gemm_kernels.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def recorded_traffic(kernel, cfg):
+    """HBM-side bytes per launch from the committed rocprofv3 --pmc summary
+    (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), or None
+    if there is none for this kernel and workload or the kernel changed."""
+    import glob
+    digest = kernel_source_digest()
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        rec = {}
+        for line in open(path):
+            if line.startswith("traffic-record:"):
+                for kv in line.split(":", 1)[1].split():
+                    k, v = kv.split("=", 1)
+                    rec[k] = v
+        if (rec.get("kernel") == kernel and rec.get("workload") == cfg["workload"].split(":")[0]
+                and rec.get("source_sha256") == digest):
+            return float(rec["bytes_per_launch"])
+    return None
 
 
 # --------------------------------------------------------------- cpu baseline
 def cpu_baseline(name):
-    """The oracle, untuned, on a bounded sample of the workload (host cores)."""
+    """The oracle, untuned, on a bounded sample of the workload (host cores):
+    the whole dense workload (about 10-20 s), or for the other workloads a
+    row sample whose flops scale the rate."""
     import workloads
     from oracle import gemm as ogemm, quant as oquant
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = 1
-    c = workloads.WORKLOADS["dense" if name not in workloads.WORKLOADS else name]
-    if name in ("moe", "decode"):
-        M, N, K = 64, c["N"], c["K"]
-        rows_w = np.arange(N)
+        cores = os.cpu_count() or 1
+    c = workloads.WORKLOADS[name]
+    if name == "dense":
+        M, N, K = c["M"], c["N"], c["K"]
+        A, W = workloads.dense_inputs(name)
+        what = "the whole dense workload"
+    elif name == "largek":
+        M, N, K = 64, 512, c["K"]
+        A, W = workloads.dense_inputs(name, rows_a=np.arange(M), rows_w=np.arange(N))
+        what = f"rows 0..{M - 1} of A and 0..{N - 1} of W"
     else:
-        M, N, K = 32, min(c["N"], 4096), min(c["K"], 7168)
-        rows_w = np.arange(N)
-    if "M" in c:
-        A, W = workloads.dense_inputs(name, rows_a=np.arange(M), rows_w=rows_w)
-        A, W = A[:, :K], W[:, :K]
-    else:
-        A = workloads.act_rows(np.arange(M), K, c["seed"])
-        W = workloads.weight_rows(rows_w, K, c["seed"], c["w_std"])
+        M, N, K = 256, c["N"], c["K"]
+        outl = workloads.outlier_channels(K, c["seed"], c["outlier_frac"], c["outlier_count"])
+        A = workloads.act_rows(np.arange(M), K, c["seed"], c["act_std"], outl, c["outlier_mult"])
+        W = workloads.weight_rows(np.arange(N), K, c["seed"], c["w_std"])
+        what = f"{M} activation rows x one expert's {N}x{K} weight"
     t0 = time.perf_counter()
     qa, sa = oquant.quantize_act(A)
     qw, sw = oquant.quantize_weight(W)
@@ -189,8 +242,8 @@ def cpu_baseline(name):
     dt = time.perf_counter() - t0
     flops = 2.0 * M * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle quantize_act({M}x{K}) + quantize_weight({N}x{K}) + exact float64 "
-                      f"per-chunk GEMM {M}x{N}x{K}; {dt:.1f} s wall; value = 2*M*N*K / wall"}
+            "sample": f"{what}: oracle quantize_act({M}x{K}) + quantize_weight({N}x{K}) + exact "
+                      f"float64 per-chunk GEMM {M}x{N}x{K}; {dt:.1f} s wall; value = 2*M*N*K / wall"}
 
 
 # ----------------------------------------------------------------------- main
@@ -200,70 +253,71 @@ def main():
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     import torch
     import fine_grained_block_fp8q_amd as fq
 
     sets = args.sets or (4 if args.workload in ("dense",) else 2 if args.workload == "decode" else 1)
     if args.workload in ("dense", "largek"):
-        step, kernels, flops, cfg, _, shape = setup_dense(fq, torch, args.workload, sets)
+        step, launch, kernels, flops, cfg = setup_dense(fq, torch, args.workload, sets)
     else:
-        step, kernels, flops, cfg, _, shape = setup_grouped(fq, torch, args.workload, sets)
+        step, launch, kernels, flops, cfg = setup_grouped(fq, torch, args.workload, sets)
     torch.cuda.synchronize()
 
-    nev = 4
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+    # Timed region: exactly `steps` steps, synchronized on both sides.
     for i in range(args.warmup):
-        step(i, mk())
-    torch.cuda.synchronize()
-    evs = [mk() for _ in range(args.steps)]
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nev - 1)]
-                    for i in range(args.steps)])  # ms
-    span = np.array([evs[i][0].elapsed_time(evs[i][nev - 1]) for i in range(args.steps)])
     ms_per_step = wall * 1e3 / args.steps
 
-    ktimes = {}
-    if args.workload in ("dense", "largek"):
-        ktimes = {"fp8q_quantize_act": seg[:, 0], "fp8q_quantize_weight": seg[:, 1],
-                  "fp8q_gemm": seg[:, 2]}
-    else:
-        ktimes = {"fp8q_quantize_act": seg[:, 0], "fp8q_grouped_gemm": seg[:, 2],
-                  "fp8q_grouped_gemm:flops": seg[:, 2]}
+    # Per-kernel durations: HIP events on the launch stream around `steps`
+    # back-to-back launches of each kernel (same inputs, same launch shape).
     kout = {}
     for kname, bound, work, unit in kernels:
-        avg_ms = float(np.mean(ktimes[kname]))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            launch(kname, args.warmup + i)
+        e1.record()
+        torch.cuda.synchronize()
+        avg_ms = e0.elapsed_time(e1) / args.steps
         if unit == "B":
             ach = work / (avg_ms * 1e-3) / 1e9
-            kout[kname] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ktimes[kname])) * 1e3,
-                           "GB_s": ach, "frac_hbm": ach / PEAK_HBM_GBS, "bytes": work}
+            kout[kname] = {"avg_us": avg_ms * 1e3, "GB_s": ach, "frac_hbm": ach / PEAK_HBM_GBS,
+                           "bytes": work}
         else:
             ach = work / (avg_ms * 1e-3) / 1e12
-            kout[kname] = {"avg_us": avg_ms * 1e3, "median_us": float(np.median(ktimes[kname])) * 1e3,
-                           "TFLOP_s": ach, "frac_fp8_peak": ach / PEAK_FP8_TFLOPS, "flops": work}
+            kout[kname] = {"avg_us": avg_ms * 1e3, "TFLOP_s": ach,
+                           "frac_fp8_peak": ach / PEAK_FP8_TFLOPS, "flops": work}
 
     if args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm"]
+        traffic = recorded_traffic("fp8q_gemm", cfg)
         roof = {"kernel": "fp8q_gemm", "bound": "mfma", "achieved": dom["TFLOP_s"],
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": dom["TFLOP_s"] / PEAK_FP8_TFLOPS,
-                "traffic": None}
+                "traffic": traffic}
     else:
         dom = kout["fp8q_grouped_gemm"]
+        dom["TFLOP_s"] = flops / (dom["avg_us"] * 1e-6) / 1e12
+        dom["frac_fp8_peak"] = dom["TFLOP_s"] / PEAK_FP8_TFLOPS
         roof = {"kernel": "fp8q_grouped_gemm", "bound": "hbm", "achieved": dom["GB_s"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom["GB_s"] / PEAK_HBM_GBS,
-                "traffic": None}
+                "traffic": recorded_traffic("fp8q_grouped_gemm", cfg)}
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     rec = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
            "data": "synthetic (seeded; shapes and distributions of the workload table)",
-           "config": cfg, "roofline": roof, "kernels": kout,
-           "event_ms_per_step": float(np.mean(span))}
+           "config": cfg, "roofline": roof, "kernels": kout}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(args.workload)
     print(json.dumps(rec), flush=True)
