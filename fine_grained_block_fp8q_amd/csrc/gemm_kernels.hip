@@ -26,7 +26,7 @@
 
 namespace fp8q {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int ROWS_ = BM_>
 struct GemmCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -39,29 +39,35 @@ struct GemmCfg {
   static constexpr int WN = BN / WAVES_N;
   static constexpr int MB = WM / 16;                // MFMA row blocks per wave
   static constexpr int NB = WN / 16;                // MFMA column blocks per wave
-  static constexpr int A_BYTES = BM * BK;
+  static constexpr int ROWS = ROWS_;                // A rows staged per chunk (<= BM)
+  static constexpr int A_BYTES = ROWS * BK;
   static constexpr int B_BYTES = BN * BK;
   static constexpr int SA_BYTES = NWAVES * 256;     // 64 row scales per wave
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int LDS_BYTES = STAGE * STAGES;
-  static constexpr int A_INSTR = A_BYTES / 1024 / NWAVES;   // per wave per chunk
-  static constexpr int B_INSTR = B_BYTES / 1024 / NWAVES;
-  static constexpr int LOADS = A_INSTR + B_INSTR + 1;        // + the scale slot
+  static constexpr int A_BLK = A_BYTES / 1024;      // 1 KiB load instructions for A
+  static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
+  static constexpr int PER_WAVE = OP_BLK / NWAVES;  // operand loads per wave per chunk
+  static constexpr int LOADS = PER_WAVE + 1;        // + the scale slot
   static_assert(WM == 64, "a wave's rows are 64 (one 256-byte scale slot)");
   static_assert(WN == 128, "a wave's columns must be one 128-wide weight block");
-  static_assert(A_BYTES % (1024 * NWAVES) == 0 && B_BYTES % (1024 * NWAVES) == 0,
-                "tile loads must split evenly over the waves");
+  static_assert(ROWS % 64 == 0 && ROWS <= BM, "staged rows cover whole waves");
+  static_assert(OP_BLK % NWAVES == 0, "tile loads must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 2 && STAGES <= 4 && LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 6 && LOADS * (STAGES - 2) < 64, "vmcnt range");
 };
 
 // Dense configuration: 256 x 256 tiles, 8 waves (two per SIMD, so one wave's
 // promotion FMAs overlap the other's MFMAs), 2 stages (130 KiB of LDS).
 using DenseCfg = GemmCfg<256, 256, 4, 2, 2>;
-// Grouped configuration: 256-row tiles cover an expert's tokens (decode
+// Grouped configurations: 256-row tiles cover an expert's tokens (decode
 // batches hold at most 256) so each expert's weights stream once per n-tile.
-using GroupedCfg = GemmCfg<256, 128, 4, 1, 3>;
+// Only the tile's live rows (rounded up to 64) are staged, and the LDS this
+// frees deepens the ring: 6 / 4 / 3 / 3 stages for 64 / 128 / 192 / 256 rows,
+// i.e. up to 80 KiB of weights in flight per CU.
+template <int ROWS, int S>
+using GroupedCfg = GemmCfg<256, 128, 4, 1, S, ROWS>;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -90,20 +96,59 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Wait until at most `after` chunks' loads (issued after the one needed) are
-// still outstanding for this wave.
+// still outstanding for this wave (after <= MAXA <= 4).
 template <int LOADS, int MAXA>
 __device__ __forceinline__ void wait_chunk(int after) {
-  if (MAXA >= 2 && after >= 2) wait_vmcnt<LOADS * 2>();
+  if (MAXA >= 4 && after >= 4) wait_vmcnt<LOADS * 4>();
+  else if (MAXA >= 3 && after >= 3) wait_vmcnt<LOADS * 3>();
+  else if (MAXA >= 2 && after >= 2) wait_vmcnt<LOADS * 2>();
   else if (MAXA >= 1 && after >= 1) wait_vmcnt<LOADS>();
   else wait_vmcnt<0>();
 }
 
-// Issue the direct-to-LDS loads of one K chunk (A tile, W tile, row scales).
-// Each load instruction moves 64 lanes x 16 B = 8 LDS rows of 128 B; lane i
-// of the instruction lands at LDS byte 16*i, i.e. row i/8, physical column
-// i%8, and therefore fetches logical column swz(row, i%8) from global memory.
-// Rows past the valid range are clamped to the last valid row (their results
-// are never stored).  Every wave issues exactly Cfg::LOADS instructions.
+// Issue the direct-to-LDS loads of one K chunk (A rows, W rows, row scales).
+// The operand tiles are cut into 1 KiB load instructions (8 rows of 128 B):
+// instructions 0 .. A_BLK-1 carry A rows, the rest W rows, and wave w issues
+// instructions w*PER_WAVE .. w*PER_WAVE + PER_WAVE - 1.  Lane i of an
+// instruction lands at LDS byte 16*i, i.e. row i/8, physical column i%8, and
+// therefore fetches logical column swz(row, i%8) from global memory.  Rows past
+// the valid range are clamped to the last valid row (their results are never
+// stored).  Every wave issues exactly Cfg::LOADS instructions per chunk.
+template <class Cfg>
+__device__ __forceinline__ void issue_one(uint8_t* stage, const uint8_t* __restrict__ A,
+                                          const uint8_t* __restrict__ W, int64_t a_row0,
+                                          int64_t a_rows, int64_t w_row0, int64_t w_rows,
+                                          int64_t K, int64_t g, int wave, int lane, int j) {
+  const int sub_r = lane >> 3;
+  const int pc = lane & 7;
+  const int m = wave * Cfg::PER_WAVE + j;
+  if (m < Cfg::A_BLK) {
+    const int r = m * 8 + sub_r;
+    int64_t gr = a_row0 + r;
+    gr = gr < a_rows ? gr : a_rows - 1;
+    const uint8_t* src = A + gr * K + g * Cfg::BK + swz(r, pc) * 16;
+    __builtin_amdgcn_global_load_lds(src, to_lds(stage + m * 1024), 16, 0, 0);
+  } else {
+    const int mb = m - Cfg::A_BLK;
+    const int r = mb * 8 + sub_r;
+    int64_t gr = w_row0 + r;
+    gr = gr < w_rows ? gr : w_rows - 1;
+    const uint8_t* src = W + gr * K + g * Cfg::BK + swz(r, pc) * 16;
+    __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + mb * 1024), 16, 0, 0);
+  }
+}
+
+template <class Cfg>
+__device__ __forceinline__ void issue_scales(uint8_t* stage, const float* __restrict__ SA,
+                                             int64_t a_row0, int64_t a_rows, int64_t sa_ld,
+                                             int64_t g, int wave, int wave_m, int lane) {
+  int64_t gr = a_row0 + wave_m * 64 + lane;
+  gr = gr < a_rows ? gr : a_rows - 1;
+  const float* src = SA + g * sa_ld + gr;
+  __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256),
+                                   4, 0, 0);
+}
+
 template <class Cfg>
 __device__ __forceinline__ void issue_chunk(uint8_t* stage, const uint8_t* __restrict__ A,
                                             const float* __restrict__ SA,
@@ -111,33 +156,10 @@ __device__ __forceinline__ void issue_chunk(uint8_t* stage, const uint8_t* __res
                                             int64_t a_rows, int64_t w_row0, int64_t w_rows,
                                             int64_t K, int64_t sa_ld, int64_t g, int wave,
                                             int wave_m, int lane) {
-  const int sub_r = lane >> 3;
-  const int pc = lane & 7;
 #pragma unroll
-  for (int j = 0; j < Cfg::A_INSTR; ++j) {
-    const int blk = wave * Cfg::A_INSTR + j;
-    const int r = blk * 8 + sub_r;
-    int64_t gr = a_row0 + r;
-    gr = gr < a_rows ? gr : a_rows - 1;
-    const uint8_t* src = A + gr * K + g * Cfg::BK + swz(r, pc) * 16;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + blk * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < Cfg::B_INSTR; ++j) {
-    const int blk = wave * Cfg::B_INSTR + j;
-    const int r = blk * 8 + sub_r;
-    int64_t gr = w_row0 + r;
-    gr = gr < w_rows ? gr : w_rows - 1;
-    const uint8_t* src = W + gr * K + g * Cfg::BK + swz(r, pc) * 16;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + blk * 1024), 16, 0, 0);
-  }
-  {  // this wave's 64 row scales
-    int64_t gr = a_row0 + wave_m * 64 + lane;
-    gr = gr < a_rows ? gr : a_rows - 1;
-    const float* src = SA + g * sa_ld + gr;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256),
-                                     4, 0, 0);
-  }
+  for (int j = 0; j < Cfg::PER_WAVE; ++j)
+    issue_one<Cfg>(stage, A, W, a_row0, a_rows, w_row0, w_rows, K, g, wave, lane, j);
+  issue_scales<Cfg>(stage, SA, a_row0, a_rows, sa_ld, g, wave, wave_m, lane);
 }
 
 // MFMA operand fragment: LDS row r, the 32-byte slice q of its 128-byte K
@@ -192,7 +214,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   const float* sw_row = t.SW + wblk * G;
 
   // Waves whose rows are all past the valid range skip the MFMA work.
-  const bool wave_live = (t.a_row0 + wave_m * Cfg::WM) < t.a_rows;
+  const bool wave_live =
+      (wave_m * Cfg::WM < Cfg::ROWS) && (t.a_row0 + wave_m * Cfg::WM) < t.a_rows;
 
   v4f acc[MB][NB];
 #pragma unroll
@@ -215,6 +238,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
       wait_chunk<Cfg::LOADS, S - 2>(left < S - 2 ? (int)left : S - 2);
     }
     lds_barrier();  // every wave's chunk g landed; chunk g-1's stage is free
+    // The loads of chunk g+S-1 go into the stage chunk g-1 used (free after
+    // the barrier).
     {
       const int64_t gn = g + S - 1;
       if (gn < G) {
@@ -240,28 +265,25 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
       mult[i] = sa * sw;
     }
     // Software pipeline over the MB x NB blocks (row block fastest, so one B
-    // fragment serves MB MFMAs): the MFMA of block k+1 is issued before the
-    // VALU folds block k's partial, so the matrix core and the VALU overlap
-    // with only two partials live; block j+1's B fragment is read from LDS
-    // while block j's MFMAs run.
+    // fragment serves MB MFMAs): block k's partial is folded by the VALU two
+    // MFMAs after it was issued, when its result is surely back, so the
+    // matrix core and the VALU overlap without dependency stalls; block j+1's
+    // B fragment is read from LDS while block j's MFMAs run.
+    constexpr int LAG = 2;
     v8i b[2];
-    v4f p[2];
+    v4f p[LAG + 1];
     b[0] = load_frag(Bs, wave_n * Cfg::WN + r16, q);
-    p[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[0], b[0], v4f{0.f, 0.f, 0.f, 0.f},
-                                                            0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int k = 1; k < MB * NB; ++k) {
-      const int i = k % MB, j = k / MB;
-      if (i == 1 && j + 1 < NB)
-        b[(j + 1) & 1] = load_frag(Bs, wave_n * Cfg::WN + (j + 1) * 16 + r16, q);
-      p[k & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          a[i], b[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      const int kp = k - 1;
-      promote(acc[kp % MB][kp / MB], p[kp & 1], mult[kp % MB]);
-    }
-    {
-      const int kp = MB * NB - 1;
-      promote(acc[kp % MB][kp / MB], p[kp & 1], mult[kp % MB]);
+    for (int k = 0; k < MB * NB + LAG; ++k) {
+      if (k < MB * NB) {
+        const int i = k % MB, j = k / MB;
+        if (i == 0 && j + 1 < NB)
+          b[(j + 1) & 1] = load_frag(Bs, wave_n * Cfg::WN + (j + 1) * 16 + r16, q);
+        p[k % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a[i], b[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      }
+      const int kp = k - LAG;
+      if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
     }
   }
 
@@ -334,19 +356,34 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
 }
 
 // Grouped variant.  The grid over-provisions tiles; each workgroup maps its id
-// to (expert, m-tile, n-tile) by a prefix sum of ceil(M_e / BM) over the device
-// offsets, held in LDS.  Workgroups past the last tile exit.
+// to (expert, m-tile, n-tile) by a prefix sum of ceil(M_e / 256) over the device
+// offsets, held in LDS.  Workgroups past the last real tile exit.  Real tiles
+// are numbered (expert, m-tile)-major, n-tile fastest, and handed to XCDs in
+// contiguous runs (workgroup id mod 8 is its XCD), so the n-tiles of one
+// expert share that expert's rows of A in one L2.  Each tile then runs the
+// instantiation for its live row count.
 constexpr int kMaxExpertsLds = 1024;
+constexpr int kGroupedThreads = 256;
+constexpr int kGroupedLds =
+    GroupedCfg<64, 6>::LDS_BYTES > GroupedCfg<128, 4>::LDS_BYTES
+        ? (GroupedCfg<64, 6>::LDS_BYTES > GroupedCfg<256, 3>::LDS_BYTES
+               ? GroupedCfg<64, 6>::LDS_BYTES
+               : GroupedCfg<256, 3>::LDS_BYTES)
+        : GroupedCfg<128, 4>::LDS_BYTES;
+static_assert(GroupedCfg<192, 3>::LDS_BYTES <= kGroupedLds, "grouped LDS sizing");
+static_assert(GroupedCfg<64, 6>::THREADS == kGroupedThreads &&
+                  GroupedCfg<256, 3>::THREADS == kGroupedThreads,
+              "all grouped configurations use the same workgroup");
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS) void grouped_gemm_kernel(
+__global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, int64_t M_total,
     const int32_t* __restrict__ off, int G, const uint8_t* __restrict__ W,
     const float* __restrict__ SW, int64_t N, int64_t K, void* __restrict__ C, int out_bf16,
     int tiles_n) {
-  constexpr int T = Cfg::THREADS;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS_BYTES];
-  static_assert((kMaxExpertsLds + 1 + T) * 4 <= Cfg::LDS_BYTES, "prefix scratch fits in LDS");
+  constexpr int T = kGroupedThreads;
+  constexpr int BM = 256;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGroupedLds];
+  static_assert((kMaxExpertsLds + 1 + T) * 4 <= kGroupedLds, "prefix scratch fits in LDS");
   int* mt_prefix = reinterpret_cast<int*>(smem);  // [G + 1], reused before the mainloop
   int* scan = mt_prefix + kMaxExpertsLds + 1;     // [T]
 
@@ -360,7 +397,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void grouped_gemm_kernel(
     int cnt = 0;
     if (e < G) {
       const int rows = off[e + 1] - off[e];
-      cnt = rows > 0 ? (rows + Cfg::BM - 1) / Cfg::BM : 0;
+      cnt = rows > 0 ? (rows + BM - 1) / BM : 0;
     }
     scan[tid] = cnt;
     __syncthreads();
@@ -374,11 +411,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void grouped_gemm_kernel(
     running += scan[T - 1];
     __syncthreads();
   }
-  const int total_mtiles = running;
-  const int tile = blockIdx.x;
-  const int mt_global = tile / tiles_n;
-  const int tn = tile % tiles_n;
-  if (mt_global >= total_mtiles) return;
+  const int total = running * tiles_n;  // real tiles
+  const int bid = blockIdx.x;
+  if (bid >= total) return;
+  // XCD-contiguous numbering of the real tiles: bid -> id is a bijection on
+  // [0, total); XCD x (= bid mod 8) receives ids [x*q + min(x, r), ...).
+  const int q8 = total / kXcds, r8 = total % kXcds;
+  const int x = bid % kXcds;
+  const int id = x * q8 + (x < r8 ? x : r8) + bid / kXcds;
+  const int mt_global = id / tiles_n;
+  const int tn = id % tiles_n;
   // expert e with prefix[e] <= mt_global < prefix[e+1]
   int lo = 0, hi = G;
   while (hi - lo > 1) {
@@ -396,16 +438,24 @@ __global__ __launch_bounds__(Cfg::THREADS) void grouped_gemm_kernel(
   t.SA = SA;
   t.W = W + (int64_t)e * N * K;
   t.SW = SW + (int64_t)e * (N / 128) * (K / 128);
-  t.a_row0 = r0 + (int64_t)mt * Cfg::BM;
+  t.a_row0 = r0 + (int64_t)mt * BM;
   t.a_rows = r1;
-  t.w_row0 = (int64_t)tn * Cfg::BN;
+  t.w_row0 = (int64_t)tn * 128;
   t.w_rows = N;
   t.K = K;
   t.sa_ld = M_total;
   t.C = C;
   t.ldc = N;
   t.out_bf16 = out_bf16;
-  gemm_tile<Cfg>(t, smem);
+  const int64_t live = r1 - t.a_row0;  // 1 .. (>= 256 when more m-tiles follow)
+  if (live <= 64)
+    gemm_tile<GroupedCfg<64, 6>>(t, smem);
+  else if (live <= 128)
+    gemm_tile<GroupedCfg<128, 4>>(t, smem);
+  else if (live <= 192)
+    gemm_tile<GroupedCfg<192, 3>>(t, smem);
+  else
+    gemm_tile<GroupedCfg<256, 3>>(t, smem);
 }
 
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
@@ -426,15 +476,14 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
                                const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
                                int64_t N, int64_t K, void* c, int out_bf16,
                                hipStream_t stream) {
-  using Cfg = GroupedCfg;
   if (M_total == 0 || N == 0) return hipSuccess;
   if (G > kMaxExpertsLds) return hipErrorInvalidValue;
-  const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
-  // sum_e ceil(M_e / BM) <= floor(M_total / BM) + G
-  const int64_t max_mtiles = M_total / Cfg::BM + G;
+  const int64_t tiles_n = (N + 127) / 128;
+  // sum_e ceil(M_e / 256) <= floor(M_total / 256) + G
+  const int64_t max_mtiles = M_total / 256 + G;
   const int64_t tiles = max_mtiles * tiles_n;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0,
+  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)tiles), dim3(kGroupedThreads), 0,
                      stream, a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16,
                      (int)tiles_n);
   return hipGetLastError();
