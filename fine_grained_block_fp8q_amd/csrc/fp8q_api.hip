@@ -112,6 +112,15 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K, uint8
   return launched(fp8q::launch_quantize_weight(w_bf16, N, K, q, s, (int)mode, stream));
 }
 
+// The GEMM kernels address a tile's operands with 32-bit buffer offsets
+// (row-in-tile * K + chunk offset) and a chunk's row scales with a 31-bit
+// scalar offset (chunk * rows * 4): K up to 2^22 and rows * K/128 * 4 below
+// 2^31 keep every offset in range.
+static bool gemm_extent_ok(int64_t rows, int64_t K) {
+  if (K > (int64_t(1) << 22)) return false;
+  return rows <= int64_t(0x7FFFFFFF) / 4 / (K / 128);
+}
+
 fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
                       const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
                       fp8q_out_dtype out, hipStream_t stream) {
@@ -126,6 +135,7 @@ fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
   if (!valid_out(out)) return FP8Q_ERR_ENUM;
   if (empty_out) return FP8Q_OK;
   if (empty_k) return FP8Q_ERR_UNSUPPORTED;  // C = 0 would need a fill kernel
+  if (!gemm_extent_ok(M, K)) return FP8Q_ERR_UNSUPPORTED;
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_gemm(a_q, a_s, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16, stream));
@@ -149,6 +159,7 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
   if (!valid_out(out)) return FP8Q_ERR_ENUM;
   if (empty_out) return FP8Q_OK;
   if (K == 0) return FP8Q_ERR_UNSUPPORTED;
+  if (!gemm_extent_ok(M_total, K)) return FP8Q_ERR_UNSUPPORTED;
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c,

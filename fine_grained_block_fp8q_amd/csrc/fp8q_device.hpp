@@ -9,6 +9,7 @@ namespace fp8q {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Largest finite OCP E4M3 magnitude: (1 + 6/8) * 2^8.
 constexpr float kE4M3Max = 448.0f;

@@ -10,17 +10,24 @@
 // MI355X mapping.  One v_mfma_f32_16x16x128_f8f6f4 consumes exactly one
 // 128-wide K chunk of a 16x16 output block, so each chunk's partial P_g is a
 // single MFMA started from zero; the promotion acc = fma(P_g, s_a*s_w, acc) is
-// four VALU FMAs per MFMA.  Inside a wave the column blocks are software
-// pipelined: the MFMAs of block j run on the matrix core while the VALU folds
-// block j-1's partials into the accumulators (the role the pages give to two
-// alternating warpgroups on Hopper).
+// four VALU FMAs per MFMA.  The product is formed transposed (C^T = W A^T:
+// MFMA rows are weight rows, MFMA columns are activation rows), so a lane's
+// four results of a block share one activation row and one multiplier, and
+// are four consecutive outputs (one 16-byte store).  Inside a wave the blocks
+// are software pipelined: block k's partial is folded by the VALU while the
+// matrix core runs the next MFMAs (the role the pages give to two alternating
+// warpgroups on Hopper).
 //
-// Each wave owns a 64 x 128 output tile: its 128 columns are one weight
-// block, so s_w is one wave-uniform scalar per chunk, and its 64 row scales are
-// one 256-byte LDS slot per chunk.  Operands move HBM/L2 -> LDS with 16-byte
-// direct-to-LDS loads (no VGPR staging) through a ring of STAGES K chunks, one
-// barrier per chunk.  LDS rows are 128 bytes (one K chunk) with the 16-byte
-// column index XOR-swizzled per row so fragment reads are bank-conflict free.
+// Each wave owns 128 weight rows x 64 activation rows: the 128 weight rows
+// are one weight block, so s_w is one wave-uniform scalar per chunk, and the
+// 64 row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
+// LDS with 16-byte direct-to-LDS buffer loads (no VGPR staging) through a ring
+// of STAGES K chunks with one barrier per chunk; the loads of the chunks ahead
+// are spread over the MFMA sequence, and the next chunk's fragments are read
+// into registers before the current chunk's last MFMAs, so the matrix core
+// does not drain at chunk boundaries.  LDS rows are 128 bytes (one K chunk)
+// with the 16-byte column index XOR-swizzled per row so fragment reads are
+// bank-conflict free.
 
 #include "fp8q_device.hpp"
 
@@ -59,7 +66,7 @@ struct GemmCfg {
 };
 
 // Dense configuration: 256 x 256 tiles, 8 waves (two per SIMD, so one wave's
-// promotion FMAs overlap the other's MFMAs), 2 stages (130 KiB of LDS).
+// promotion FMAs overlap the other's MFMAs), 2 stages (132 KiB of LDS).
 using DenseCfg = GemmCfg<256, 256, 4, 2, 2>;
 // Grouped configurations: 256-row tiles cover an expert's tokens (decode
 // batches hold at most 256) so each expert's weights stream once per n-tile.
@@ -68,6 +75,21 @@ using DenseCfg = GemmCfg<256, 256, 4, 2, 2>;
 // i.e. up to 80 KiB of weights in flight per CU.
 template <int ROWS, int S>
 using GroupedCfg = GemmCfg<256, 128, 4, 1, S, ROWS>;
+
+// Main-loop schedule constants (measured on the 4096 x 4096 x 7168 shape;
+// the result is insensitive to them within +-2%):
+//   kDma0, kDmaStep  head load d of the next chunk goes out after MFMA
+//                    kDma0 + d * kDmaStep;
+//   kPromoteLag      a block's partial is promoted this many MFMAs after it
+//                    was issued, when the matrix core has surely written it;
+//   kBPrefetch       weight fragments are read this many row blocks ahead;
+//   kBarLead         the chunk barrier sits this many MFMAs before the
+//                    chunk's last row block.
+constexpr int kDma0 = 1;
+constexpr int kDmaStep = 2;
+constexpr int kPromoteLag = 2;
+constexpr int kBPrefetch = 1;
+constexpr int kBarLead = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -95,90 +117,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most `after` chunks' loads (issued after the one needed) are
-// still outstanding for this wave (after <= MAXA <= 4).
-template <int LOADS, int MAXA>
-__device__ __forceinline__ void wait_chunk(int after) {
-  if (MAXA >= 4 && after >= 4) wait_vmcnt<LOADS * 4>();
-  else if (MAXA >= 3 && after >= 3) wait_vmcnt<LOADS * 3>();
-  else if (MAXA >= 2 && after >= 2) wait_vmcnt<LOADS * 2>();
-  else if (MAXA >= 1 && after >= 1) wait_vmcnt<LOADS>();
-  else wait_vmcnt<0>();
-}
-
-// Issue the direct-to-LDS loads of one K chunk (A rows, W rows, row scales).
-// The operand tiles are cut into 1 KiB load instructions (8 rows of 128 B):
-// instructions 0 .. A_BLK-1 carry A rows, the rest W rows, and wave w issues
-// instructions w*PER_WAVE .. w*PER_WAVE + PER_WAVE - 1.  Lane i of an
-// instruction lands at LDS byte 16*i, i.e. row i/8, physical column i%8, and
-// therefore fetches logical column swz(row, i%8) from global memory.  Rows past
-// the valid range are clamped to the last valid row (their results are never
-// stored).  Every wave issues exactly Cfg::LOADS instructions per chunk.
-template <class Cfg>
-__device__ __forceinline__ void issue_one(uint8_t* stage, const uint8_t* __restrict__ A,
-                                          const uint8_t* __restrict__ W, int64_t a_row0,
-                                          int64_t a_rows, int64_t w_row0, int64_t w_rows,
-                                          int64_t K, int64_t g, int wave, int lane, int j) {
-  const int sub_r = lane >> 3;
-  const int pc = lane & 7;
-  const int m = wave * Cfg::PER_WAVE + j;
-  if (m < Cfg::A_BLK) {
-    const int r = m * 8 + sub_r;
-    int64_t gr = a_row0 + r;
-    gr = gr < a_rows ? gr : a_rows - 1;
-    const uint8_t* src = A + gr * K + g * Cfg::BK + swz(r, pc) * 16;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + m * 1024), 16, 0, 0);
-  } else {
-    const int mb = m - Cfg::A_BLK;
-    const int r = mb * 8 + sub_r;
-    int64_t gr = w_row0 + r;
-    gr = gr < w_rows ? gr : w_rows - 1;
-    const uint8_t* src = W + gr * K + g * Cfg::BK + swz(r, pc) * 16;
-    __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + mb * 1024), 16, 0, 0);
-  }
-}
-
-template <class Cfg>
-__device__ __forceinline__ void issue_scales(uint8_t* stage, const float* __restrict__ SA,
-                                             int64_t a_row0, int64_t a_rows, int64_t sa_ld,
-                                             int64_t g, int wave, int wave_m, int lane) {
-  int64_t gr = a_row0 + wave_m * 64 + lane;
-  gr = gr < a_rows ? gr : a_rows - 1;
-  const float* src = SA + g * sa_ld + gr;
-  __builtin_amdgcn_global_load_lds(src, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256),
-                                   4, 0, 0);
-}
-
-template <class Cfg>
-__device__ __forceinline__ void issue_chunk(uint8_t* stage, const uint8_t* __restrict__ A,
-                                            const float* __restrict__ SA,
-                                            const uint8_t* __restrict__ W, int64_t a_row0,
-                                            int64_t a_rows, int64_t w_row0, int64_t w_rows,
-                                            int64_t K, int64_t sa_ld, int64_t g, int wave,
-                                            int wave_m, int lane) {
-#pragma unroll
-  for (int j = 0; j < Cfg::PER_WAVE; ++j)
-    issue_one<Cfg>(stage, A, W, a_row0, a_rows, w_row0, w_rows, K, g, wave, lane, j);
-  issue_scales<Cfg>(stage, SA, a_row0, a_rows, sa_ld, g, wave, wave_m, lane);
-}
-
-// MFMA operand fragment: LDS row r, the 32-byte slice q of its 128-byte K
-// chunk (two swizzled 16-byte columns).  A and B fragments use the same
-// (q, byte) -> K mapping, so every product pairs matching K indices.
-__device__ __forceinline__ v8i load_frag(const uint8_t* base, int r, int q) {
-  const v4i lo = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, 2 * q) * 16);
-  const v4i hi = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, 2 * q + 1) * 16);
-  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// Promotion of one 16x16 chunk partial: acc += P * (s_a[row] * s_w).
-__device__ __forceinline__ void promote(v4f& acc, const v4f& p, const v4f& mult) {
-  acc[0] = __builtin_fmaf(p[0], mult[0], acc[0]);
-  acc[1] = __builtin_fmaf(p[1], mult[1], acc[1]);
-  acc[2] = __builtin_fmaf(p[2], mult[2], acc[2]);
-  acc[3] = __builtin_fmaf(p[3], mult[3], acc[3]);
-}
-
 struct TileArgs {
   const uint8_t* A;     // rows of A (absolute row index)
   const float* SA;      // SA[g * sa_ld + row]
@@ -195,6 +133,100 @@ struct TileArgs {
   int out_bf16;
 };
 
+// Buffer resource over [base, base + bytes) for raw loads (gfx9 word 3:
+// 32-bit untyped data); offsets past `bytes` read as zero instead of faulting.
+constexpr int kRawRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes < 0xFFFFFFFFll ? (uint32_t)bytes : 0xFFFFFFFFu;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
+                                           kRawRsrcWord3);
+}
+
+// Direct-to-LDS loads of one K chunk (A rows, W rows, row scales).  The
+// operand tiles are cut into 1 KiB load instructions (8 rows of 128 B):
+// instructions 0 .. A_BLK-1 carry A rows, the rest W rows, and wave w issues
+// instructions w*PER_WAVE .. w*PER_WAVE + PER_WAVE - 1, then one 256-byte
+// slot of its 64 row scales: Cfg::LOADS instructions per wave per chunk.  Lane
+// i of an instruction lands at LDS byte 16*i, i.e. row i/8, physical column
+// i%8, and so fetches logical column swz(row, i%8).  Rows past the valid range
+// are clamped to the last valid row (their results are never stored).
+//
+// Addresses are buffer offsets: a scalar resource per operand based at the
+// tile's first row, a per-lane 32-bit offset fixed for the whole tile, and the
+// chunk's K offset as the scalar soffset, so issuing a load costs no VALU.
+template <class Cfg>
+struct ChunkLoader {
+  __amdgpu_buffer_rsrc_t ra, rw, rs;
+  uint32_t voff[Cfg::PER_WAVE];
+  uint32_t voff_s;
+  int64_t s_stride;  // bytes between consecutive chunks' row scales
+  int wave;
+
+  __device__ __forceinline__ void init(const TileArgs& t, int wave_, int wave_m, int lane) {
+    wave = wave_;
+    const int64_t a_live = t.a_rows - t.a_row0;  // >= 1
+    const int64_t w_live = t.w_rows - t.w_row0;  // >= 1
+    ra = make_rsrc(t.A + t.a_row0 * t.K, a_live * t.K);
+    rw = make_rsrc(t.W + t.w_row0 * t.K, w_live * t.K);
+    const int64_t G = t.K / Cfg::BK;
+    rs = make_rsrc(t.SA + t.a_row0, (G * t.sa_ld - t.a_row0) * 4);
+    s_stride = t.sa_ld * 4;
+    const int sub_r = lane >> 3;
+    const int pc = lane & 7;
+#pragma unroll
+    for (int j = 0; j < Cfg::PER_WAVE; ++j) {
+      const int m = wave * Cfg::PER_WAVE + j;
+      const bool is_a = m < Cfg::A_BLK;
+      const int r = (is_a ? m : m - Cfg::A_BLK) * 8 + sub_r;
+      const int64_t live = is_a ? a_live : w_live;
+      const int64_t rr = r < live ? r : live - 1;
+      voff[j] = (uint32_t)(rr * t.K) + (uint32_t)(swz(r, pc) * 16);
+    }
+    // Lane i of the scale load fetches row (i & 3) * 16 + i / 4 of the wave's
+    // 64 rows, so the four scales an MFMA column lane needs (rows c, 16 + c,
+    // 32 + c, 48 + c) sit side by side in LDS.
+    const int64_t rs_row = wave_m * 64 + (lane & 3) * 16 + (lane >> 2);
+    voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
+  }
+
+  // Load d (0 .. LOADS-1) of chunk g into `stage`.
+  __device__ __forceinline__ void issue(uint8_t* stage, int64_t g, int d) const {
+    if (d < Cfg::PER_WAVE) {
+      const int m = wave * Cfg::PER_WAVE + d;
+      const bool is_a = m < Cfg::A_BLK;
+      const int dst = is_a ? m * 1024 : Cfg::A_BYTES + (m - Cfg::A_BLK) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rw, to_lds(stage + dst), 16, voff[d],
+                                               (int)(g * Cfg::BK), 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256), 4, voff_s,
+          (int)(g * s_stride), 0, 0);
+    }
+  }
+};
+
+// MFMA operand fragment: LDS row r, 16-byte pieces q and q+4 of its 128-byte
+// K chunk.  A and B fragments use the same (q, byte) -> K mapping, so every
+// product pairs matching K indices, and each 8-byte group the matrix core
+// sums together is still 8 consecutive K.  Pieces (q, q+4) rather than
+// (2q, 2q+1): with the row swizzle swz, the 64 lanes of each read then
+// spread over all LDS banks in every lane group the LDS serves together
+// (measured: 1.55x the read throughput of the (2q, 2q+1) assignment).
+__device__ __forceinline__ v8i load_frag(const uint8_t* base, int r, int q) {
+  const v4i lo = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, q) * 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, q + 4) * 16);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Promotion of one 16x16 chunk partial: acc += P * (s_a[row] * s_w).
+__device__ __forceinline__ void promote(v4f& acc, const v4f& p, float mult) {
+  acc[0] = __builtin_fmaf(p[0], mult, acc[0]);
+  acc[1] = __builtin_fmaf(p[1], mult, acc[1]);
+  acc[2] = __builtin_fmaf(p[2], mult, acc[2]);
+  acc[3] = __builtin_fmaf(p[3], mult, acc[3]);
+}
+
+
 // Computes one BM x BN output tile.  All lanes of the workgroup call it.
 template <class Cfg>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
@@ -203,8 +235,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_m = wave / Cfg::WAVES_N;
   const int wave_n = wave % Cfg::WAVES_N;
-  const int r16 = lane & 15;   // fragment row (A) / column (B) within a 16-block
-  const int q = lane >> 4;     // which 32-byte slice of the 128-byte chunk
+  const int r16 = lane & 15;   // fragment row within a 16-row block
+  const int q = lane >> 4;     // which 16-byte piece pair of the 128-byte chunk
   const int64_t G = t.K / Cfg::BK;
 
   // Weight-scale row of this wave's 128 columns.
@@ -217,93 +249,167 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   const bool wave_live =
       (wave_m * Cfg::WM < Cfg::ROWS) && (t.a_row0 + wave_m * Cfg::WM) < t.a_rows;
 
+  // acc[i][j]: activation row block i (16 rows) x weight row block j.
   v4f acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Schedule of one chunk g (k = MFMA index, LAG = promotion lag):
+  //   k = 0 ..         MFMAs of chunk g; the head loads of chunk g+S-1 go out
+  //                    one every kDmaStep MFMAs from k = kDma0;
+  //   k = kBar         wait for chunk g+1's loads, barrier: every wave has
+  //                    finished reading stage g (its last weight fragment was
+  //                    read at k = MB*(NB-1-BPF)) and chunk g+1 is in LDS;
+  //   k > kBar         the tail loads of chunk g+S go into stage g, one per
+  //                    MFMA, and once a fragment register has served its last
+  //                    MFMA of chunk g it is refilled with chunk g+1's data,
+  //                    so chunk g+1 starts with its operands in registers.
+  // Step k is MFMA (weight row block j = k / MB, activation block i = k % MB):
+  // one weight fragment serves MB consecutive MFMAs.
+  // The matrix core therefore never waits for a chunk boundary: a wave that
+  // arrives early at the barrier leaves the matrix core to its SIMD partner.
+  constexpr int LAG = kPromoteLag;
+  constexpr int KSTEPS = MB * NB + LAG;
+  constexpr int kBar = MB * (NB - 1) - kBarLead;   // before the last row block
+  constexpr int TAIL = KSTEPS - 1 - kBar;          // loads issued after the barrier
+  constexpr int D1 = TAIL < Cfg::LOADS ? TAIL : Cfg::LOADS;
+  // Weight fragments are read BPF row blocks ahead into a ring of BPF+1 slots.
+  constexpr int BPF = kBPrefetch;
+  constexpr int NBUF = BPF + 1;
+  static_assert(kBar > MB * (NB - 1 - BPF), "the barrier follows the last weight read");
+  static_assert(kBar < MB * (NB - 1), "the barrier precedes the last row block");
+  // Step after which weight slot t (t < BPF) is free for chunk g+1's block t: the
+  // last MFMA of the last block j < NB with j % NBUF == t, but not before the
+  // barrier.
+  auto next_b_step = [](int t) constexpr {
+    int jt = t;
+    while (jt + NBUF < NB) jt += NBUF;
+    const int kt = MB * jt + MB - 1;
+    return kt > kBar ? kt : kBar;
+  };
+  static_assert(kDma0 + (Cfg::LOADS - D1 - 1) * kDmaStep < kBar,
+                "head loads are issued before the barrier");
+
+  ChunkLoader<Cfg> ld;
+  ld.init(t, wave, wave_m, lane);
+  // Chunk indices past the end are clamped to the last chunk: the extra loads
+  // re-fetch L2-resident bytes into a stage nobody reads again, and keep the
+  // number of loads in flight the same every iteration.
+  const int64_t g_last = G - 1;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
-    if (s < G)
-      issue_chunk<Cfg>(smem + s * Cfg::STAGE, t.A, t.SA, t.W, t.a_row0, t.a_rows, t.w_row0,
-                       t.w_rows, t.K, t.sa_ld, s, wave, wave_m, lane);
-
-  int cur_stage = 0;
-  for (int64_t g = 0; g < G; ++g) {
-    // This wave's loads of chunk g have landed once at most the chunks issued
-    // after it (up to S-2 of them) are still outstanding.
-    {
-      const int64_t left = G - 1 - g;
-      wait_chunk<Cfg::LOADS, S - 2>(left < S - 2 ? (int)left : S - 2);
-    }
-    lds_barrier();  // every wave's chunk g landed; chunk g-1's stage is free
-    // The loads of chunk g+S-1 go into the stage chunk g-1 used (free after
-    // the barrier).
-    {
-      const int64_t gn = g + S - 1;
-      if (gn < G) {
-        int st = cur_stage + S - 1;
-        st = st >= S ? st - S : st;
-        issue_chunk<Cfg>(smem + st * Cfg::STAGE, t.A, t.SA, t.W, t.a_row0, t.a_rows, t.w_row0,
-                         t.w_rows, t.K, t.sa_ld, gn, wave, wave_m, lane);
-      }
-    }
-    const uint8_t* As = smem + cur_stage * Cfg::STAGE;
-    const uint8_t* Bs = As + Cfg::A_BYTES;
-    const float* SAs = reinterpret_cast<const float*>(As + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256);
-    cur_stage = cur_stage + 1 == S ? 0 : cur_stage + 1;
-    if (!wave_live) continue;
-
-    const float sw = sw_row[g];
-    v8i a[MB];
-    v4f mult[MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      a[i] = load_frag(As, wave_m * Cfg::WM + i * 16 + r16, q);
-      const v4f sa = *reinterpret_cast<const v4f*>(SAs + i * 16 + 4 * q);
-      mult[i] = sa * sw;
-    }
-    // Software pipeline over the MB x NB blocks (row block fastest, so one B
-    // fragment serves MB MFMAs): block k's partial is folded by the VALU two
-    // MFMAs after it was issued, when its result is surely back, so the
-    // matrix core and the VALU overlap without dependency stalls; block j+1's
-    // B fragment is read from LDS while block j's MFMAs run.
-    constexpr int LAG = 2;
-    v8i b[2];
-    v4f p[LAG + 1];
-    b[0] = load_frag(Bs, wave_n * Cfg::WN + r16, q);
+    for (int d = 0; d < Cfg::LOADS; ++d)
+      ld.issue(smem + s * Cfg::STAGE, s < g_last ? s : g_last, d);
 #pragma unroll
-    for (int k = 0; k < MB * NB + LAG; ++k) {
-      if (k < MB * NB) {
-        const int i = k % MB, j = k / MB;
-        if (i == 0 && j + 1 < NB)
-          b[(j + 1) & 1] = load_frag(Bs, wave_n * Cfg::WN + (j + 1) * 16 + r16, q);
-        p[k % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            a[i], b[j & 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      }
-      const int kp = k - LAG;
-      if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
-    }
+  for (int d = 0; d < D1; ++d)
+    ld.issue(smem + (S - 1) * Cfg::STAGE, S - 1 < g_last ? S - 1 : g_last, d);
+  wait_vmcnt<Cfg::LOADS * (S - 2) + D1>();  // chunk 0 landed
+  lds_barrier();
+
+  v8i a[MB];     // activation fragments of the chunk (MFMA B operand)
+  v8i b[NBUF];   // weight fragments, a ring over row blocks (MFMA A operand)
+  if (wave_live) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) a[i] = load_frag(smem, wave_m * Cfg::WM + i * 16 + r16, q);
+#pragma unroll
+    for (int t = 0; t < BPF; ++t)
+      b[t] = load_frag(smem + Cfg::A_BYTES, wave_n * Cfg::WN + t * 16 + r16, q);
   }
 
-  // Epilogue: lane holds rows 4q..4q+3, column r16 of every 16x16 block.
+  int cur = 0;  // stage of chunk g
+  for (int64_t g = 0; g < G; ++g) {
+    const int nxt = cur + 1 == S ? 0 : cur + 1;    // stage of chunk g+1
+    const int head = cur == 0 ? S - 1 : cur - 1;   // stage of chunk g+S-1
+    const int64_t g_head = g + S - 1 < g_last ? g + S - 1 : g_last;
+    const int64_t g_tail = g + S < g_last ? g + S : g_last;
+    uint8_t* const st_cur = smem + cur * Cfg::STAGE;
+    uint8_t* const st_nxt = smem + nxt * Cfg::STAGE;
+    uint8_t* const st_head = smem + head * Cfg::STAGE;
+    if (!wave_live) {
+#pragma unroll
+      for (int d = D1; d < Cfg::LOADS; ++d) ld.issue(st_head, g_head, d);
+      wait_vmcnt<Cfg::LOADS * (S - 2)>();
+      lds_barrier();
+#pragma unroll
+      for (int d = 0; d < D1; ++d) ld.issue(st_cur, g_tail, d);
+      cur = nxt;
+      continue;
+    }
+
+    const uint8_t* Bs = st_cur + Cfg::A_BYTES;
+    const float* SAs =
+        reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256);
+    const float sw = sw_row[g];
+    const v4f sa = *reinterpret_cast<const v4f*>(SAs + 4 * r16);
+    float mult[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) mult[i] = sa[i] * sw;
+    v4f p[LAG + 1];
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      if (k < MB * NB) {
+        const int i = k % MB, j = k / MB;
+        if (i == 0 && j + BPF < NB)
+          b[(j + BPF) % NBUF] = load_frag(Bs, wave_n * Cfg::WN + (j + BPF) * 16 + r16, q);
+        p[k % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            b[j % NBUF], a[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int d = D1; d < Cfg::LOADS; ++d)
+        if (k == kDma0 + (d - D1) * kDmaStep) ld.issue(st_head, g_head, d);
+      if (k == kBar) {
+        wait_vmcnt<Cfg::LOADS * (S - 2)>();  // chunk g+1 landed
+        lds_barrier();
+      }
+      if (k < MB * NB) {
+        // Chunk g+1's fragments go into registers as soon as their chunk-g
+        // contents have served their last MFMA (and the barrier at kBar has
+        // made chunk g+1 visible): a[i] after row block NB-1's MFMA i, weight slot t
+        // after the last block of chunk g that uses it.
+        const int i = k % MB, j = k / MB;
+        if (j == NB - 1) a[i] = load_frag(st_nxt, wave_m * Cfg::WM + i * 16 + r16, q);
+#pragma unroll
+        for (int t = 0; t < BPF; ++t)
+          if (k == next_b_step(t))
+            b[t] = load_frag(st_nxt + Cfg::A_BYTES, wave_n * Cfg::WN + t * 16 + r16, q);
+      }
+#pragma unroll
+      for (int d = 0; d < D1; ++d)
+        if (k == kBar + 1 + d) ld.issue(st_cur, g_tail, d);
+      // Keep the step order: MFMA k is issued before block k-LAG's
+      // promotion.  Left free, the scheduler hoists the promotion above the
+      // MFMA (to hand its result registers to MFMA k), which leaves it right
+      // behind MFMA k-LAG+1 and stalls the wave on the matrix core's result.
+      __builtin_amdgcn_sched_barrier(0);
+      const int kp = k - LAG;
+      if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
+  }
+  wait_vmcnt<0>();  // the trailing (clamped) loads have landed before the waves exit
+
+  // Epilogue: in block (i, j) the lane holds activation row m = 16i + r16 and
+  // weight rows n = 16j + 4q .. 16j + 4q + 3, i.e. 4 consecutive outputs.
   if (!wave_live) return;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
+    const int64_t m = t.a_row0 + wave_m * Cfg::WM + i * 16 + r16;
+    if (m >= t.a_rows) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t row = t.a_row0 + wave_m * Cfg::WM + i * 16 + 4 * q + v;
-      if (row >= t.a_rows) continue;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int64_t col = t.w_row0 + wave_n * Cfg::WN + j * 16 + r16;
-        if (col >= t.w_rows) continue;
-        if (t.out_bf16)
-          reinterpret_cast<uint16_t*>(t.C)[row * t.ldc + col] =
-              (uint16_t)f32_to_bf16_bits(acc[i][j][v]);
-        else
-          reinterpret_cast<float*>(t.C)[row * t.ldc + col] = acc[i][j][v];
+    for (int j = 0; j < NB; ++j) {
+      const int64_t n = t.w_row0 + wave_n * Cfg::WN + j * 16 + 4 * q;
+      if (n >= t.w_rows) continue;
+      if (t.out_bf16) {
+        uint2 o;
+        o.x = f32_to_bf16_bits(acc[i][j][0]) | (f32_to_bf16_bits(acc[i][j][1]) << 16);
+        o.y = f32_to_bf16_bits(acc[i][j][2]) | (f32_to_bf16_bits(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(t.C) + m * t.ldc + n) = o;
+      } else {
+        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(t.C) + m * t.ldc + n) = acc[i][j];
       }
     }
   }
