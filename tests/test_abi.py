@@ -101,6 +101,10 @@ def test_gemm_validation(lib):
     assert f(A, A, A, A, 4, 128, 128, A + 8, 0, None) == E_ALIGN
     assert f(A, A, A, A, 4, 128, 128, A, 3, None) == E_ENUM
     assert f(None, None, None, None, 0, 128, 128, None, 0, None) == OK
+    # valid requests outside this build's range (host-side, before any device call)
+    assert f(A, A, A, A, 4, 128, 0, A, 0, None) == E_UNSUP            # K == 0: C = 0
+    assert f(A, A, A, A, 4, 128, (1 << 22) + 128, A, 0, None) == E_UNSUP
+    assert f(A, A, A, A, 1 << 29, 128, 128, A, 0, None) == E_UNSUP    # scale offsets >= 2^31
 
 
 def test_grouped_gemm_validation(lib):
@@ -113,6 +117,8 @@ def test_grouped_gemm_validation(lib):
     assert f(A, A, 8, A + 2, 2, A, A, 128, 128, A, 0, None) == E_ALIGN
     assert f(A, A, 8, A, 2, A, A, 128, 128, A, 5, None) == E_ENUM
     assert f(A, A, 8, A, 2000, A, A, 128, 128, A, 0, None) == E_UNSUP
+    assert f(A, A, 8, A, 2, A, A, 128, 0, A, 0, None) == E_UNSUP
+    assert f(A, A, 8, A, 2, A, A, 128, (1 << 22) + 128, A, 0, None) == E_UNSUP
     assert f(None, None, 0, A, 2, None, None, 128, 128, None, 0, None) == OK
 
 
