@@ -87,6 +87,17 @@ def dense_inputs(name, rows_a=None, rows_w=None):
     return A, W
 
 
+def rows_threaded(gen, rows, *args, threads=8):
+    """gen(rows, *args) over row blocks on a thread pool (the per-row seeding
+    makes the result independent of the split)."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.asarray(rows, dtype=np.int64)
+    parts = np.array_split(rows, max(1, min(len(rows), threads * 4)))
+    with ThreadPoolExecutor(threads) as ex:
+        out = list(ex.map(lambda r: gen(r, *args), parts))
+    return np.concatenate(out, axis=0)
+
+
 def moe_routing(tokens, experts, topk, seed):
     """Top-k routing from N(0,1) logits (ties to the lower expert index).
 
