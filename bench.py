@@ -181,12 +181,18 @@ def setup_grouped(fq, torch, name, sets):
 
 
 # -------------------------------------------------------- recorded traffic
+GEMM_SOURCES = ("gemm_kernels.hip", "gemm_common.hpp", "fp8q_device.hpp")
+
+
 def kernel_source_digest():
-    """sha256 of the GEMM kernel source: traffic figures recorded under
-    profiles/ are reported only while the kernel is unchanged."""
+    """sha256 over the GEMM kernels' sources (in GEMM_SOURCES order): traffic
+    figures recorded under profiles/ are reported only while they are
+    unchanged."""
     import hashlib
-    path = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "csrc", "gemm_kernels.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, "fine_grained_block_fp8q_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def recorded_traffic(kernel, cfg):

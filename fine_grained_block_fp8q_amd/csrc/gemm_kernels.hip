@@ -18,9 +18,9 @@
 // matrix core runs the next MFMAs (the role the pages give to two alternating
 // warpgroups on Hopper).
 //
-// Each wave owns 128 weight rows x 64 activation rows: the 128 weight rows
-// are one weight block, so s_w is one wave-uniform scalar per chunk, and the
-// 64 row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
+// Each wave owns 64 activation rows and 128 (dense) or 64 (grouped) weight
+// rows inside one 128-row weight block, so s_w is one wave-uniform scalar per
+// chunk, and the 64 row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
 // LDS with 16-byte direct-to-LDS buffer loads (no VGPR staging) through a ring
 // of STAGES K chunks with one barrier per chunk; the loads of the chunks ahead
 // are spread over the MFMA sequence, and the next chunk's fragments are read
@@ -29,7 +29,7 @@
 // with the 16-byte column index XOR-swizzled per row so fragment reads are
 // bank-conflict free.
 
-#include "fp8q_device.hpp"
+#include "gemm_common.hpp"
 
 namespace fp8q {
 
@@ -58,7 +58,7 @@ struct GemmCfg {
   static constexpr int PER_WAVE = OP_BLK / NWAVES;  // operand loads per wave per chunk
   static constexpr int LOADS = PER_WAVE + 1;        // + the scale slot
   static_assert(WM == 64, "a wave's rows are 64 (one 256-byte scale slot)");
-  static_assert(WN == 128, "a wave's columns must be one 128-wide weight block");
+  static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
   static_assert(ROWS % 64 == 0 && ROWS <= BM, "staged rows cover whole waves");
   static_assert(OP_BLK % NWAVES == 0, "tile loads must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -72,9 +72,11 @@ using DenseCfg = GemmCfg<256, 256, 4, 2, 2>;
 // batches hold at most 256) so each expert's weights stream once per n-tile.
 // Only the tile's live rows (rounded up to 64) are staged, and the LDS this
 // frees deepens the ring: 6 / 4 / 3 / 3 stages for 64 / 128 / 192 / 256 rows,
-// i.e. up to 80 KiB of weights in flight per CU.
+// i.e. up to 80 KiB of weights in flight per CU.  8 waves of 64 x 64 (two
+// per SIMD) rather than 4 of 64 x 128: a tile with few live rows still keeps
+// every SIMD busy, and each SIMD has a second wave to cover its stalls.
 template <int ROWS, int S>
-using GroupedCfg = GemmCfg<256, 128, 4, 1, S, ROWS>;
+using GroupedCfg = GemmCfg<256, 128, 4, 2, S, ROWS>;
 
 // Main-loop schedule constants (measured on the 4096 x 4096 x 7168 shape;
 // the result is insensitive to them within +-2%):
@@ -90,57 +92,6 @@ constexpr int kDmaStep = 2;
 constexpr int kPromoteLag = 2;
 constexpr int kBPrefetch = 1;
 constexpr int kBarLead = 2;
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ lds_ptr_t to_lds(uint8_t* p) { return (lds_ptr_t)(p); }
-
-// Physical 16-byte column of logical column c in LDS row r.  A fragment read
-// has 16 lanes on 16 consecutive 128-byte rows at one logical column.  With
-// f(r) = (r/2 mod 8) ^ 4*(r&1), the 8 even rows and the 8 odd rows each take
-// all 8 columns, so the 16 lanes hit 16 distinct 16-byte slots of a 256-byte
-// bank window, and each 8-row half also takes 8 distinct columns: the
-// ds_read_b128 is bank-conflict free with 32 or 64 four-byte banks.  XOR with
-// a per-row constant is an involution, so the same map locates and fetches.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (((r >> 1) & 7) ^ ((r & 1) << 2)); }
-
-// s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their maxima (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that orders LDS accesses but does not drain global loads
-// still in flight (those are waited for explicitly with vmcnt).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-struct TileArgs {
-  const uint8_t* A;     // rows of A (absolute row index)
-  const float* SA;      // SA[g * sa_ld + row]
-  const uint8_t* W;     // [w_rows][K]
-  const float* SW;      // [w_rows/128][K/128]
-  int64_t a_row0;       // first A row of the tile
-  int64_t a_rows;       // exclusive end of the valid A rows
-  int64_t w_row0;       // first W row (= output column) of the tile
-  int64_t w_rows;       // N
-  int64_t K;
-  int64_t sa_ld;        // leading dimension of SA (total rows)
-  void* C;              // output base
-  int64_t ldc;          // N
-  int out_bf16;
-};
-
-// Buffer resource over [base, base + bytes) for raw loads (gfx9 word 3:
-// 32-bit untyped data); offsets past `bytes` read as zero instead of faulting.
-constexpr int kRawRsrcWord3 = 0x00020000;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const uint32_t n = bytes < 0xFFFFFFFFll ? (uint32_t)bytes : 0xFFFFFFFFu;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n,
-                                           kRawRsrcWord3);
-}
 
 // Direct-to-LDS loads of one K chunk (A rows, W rows, row scales).  The
 // operand tiles are cut into 1 KiB load instructions (8 rows of 128 B):
@@ -205,19 +156,6 @@ struct ChunkLoader {
   }
 };
 
-// MFMA operand fragment: LDS row r, 16-byte pieces q and q+4 of its 128-byte
-// K chunk.  A and B fragments use the same (q, byte) -> K mapping, so every
-// product pairs matching K indices, and each 8-byte group the matrix core
-// sums together is still 8 consecutive K.  Pieces (q, q+4) rather than
-// (2q, 2q+1): with the row swizzle swz, the 64 lanes of each read then
-// spread over all LDS banks in every lane group the LDS serves together
-// (measured: 1.55x the read throughput of the (2q, 2q+1) assignment).
-__device__ __forceinline__ v8i load_frag(const uint8_t* base, int r, int q) {
-  const v4i lo = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, q) * 16);
-  const v4i hi = *reinterpret_cast<const v4i*>(base + r * 128 + swz(r, q + 4) * 16);
-  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
 // Promotion of one 16x16 chunk partial: acc += P * (s_a[row] * s_w).
 __device__ __forceinline__ void promote(v4f& acc, const v4f& p, float mult) {
   acc[0] = __builtin_fmaf(p[0], mult, acc[0]);
@@ -239,7 +177,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   const int q = lane >> 4;     // which 16-byte piece pair of the 128-byte chunk
   const int64_t G = t.K / Cfg::BK;
 
-  // Weight-scale row of this wave's 128 columns.
+  // Weight-scale row of this wave's weight rows (one 128-row block).
   int64_t wblk = (t.w_row0 + wave_n * Cfg::WN) / 128;
   const int64_t last_wblk = t.w_rows / 128 - 1;
   wblk = wblk < last_wblk ? wblk : last_wblk;
@@ -415,27 +353,6 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   }
 }
 
-// Workgroup id -> output tile.  Workgroups are dispatched round-robin over
-// the 8 XCDs (id mod 8), each with its own L2.  Give each XCD a contiguous
-// run of tile ids, and walk tiles in groups of kGroupM tile rows (tile row
-// fastest), so an XCD's tiles form a compact kGroupM x (run / kGroupM) block
-// that shares A row bands and W column bands in that XCD's L2.
-constexpr int kXcds = 8;
-constexpr int kGroupM = 4;
-
-__device__ __forceinline__ void xcd_tile(int bid, int nblocks, int tiles_n, int& tm, int& tn) {
-  int id = bid;
-  if (nblocks % kXcds == 0) id = (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
-  const int tiles_m = nblocks / tiles_n;
-  const int per_group = kGroupM * tiles_n;
-  const int grp = id / per_group;
-  const int first_m = grp * kGroupM;
-  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
-  const int in = id - grp * per_group;
-  tm = first_m + in % gm;
-  tn = in / gm;
-}
-
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, const uint8_t* __restrict__ W,
@@ -469,7 +386,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
 // expert share that expert's rows of A in one L2.  Each tile then runs the
 // instantiation for its live row count.
 constexpr int kMaxExpertsLds = 1024;
-constexpr int kGroupedThreads = 256;
+constexpr int kGroupedThreads = 512;
 constexpr int kGroupedLds =
     GroupedCfg<64, 6>::LDS_BYTES > GroupedCfg<128, 4>::LDS_BYTES
         ? (GroupedCfg<64, 6>::LDS_BYTES > GroupedCfg<256, 3>::LDS_BYTES
