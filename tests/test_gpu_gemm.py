@@ -202,3 +202,16 @@ def test_grouped_decode_workload_sampled():
             rows = np.sort(np.random.default_rng(e).choice(rows, 24, replace=False))
         assert_gemm_close(ch[rows], qa[rows], sa[:, rows], qw, sw, out="bf16", model_rows=2,
                           what=f"decode expert {e}")
+
+
+def test_grouped_determinism_all_tile_configs():
+    """Repeated launches are bitwise identical, with experts of every staged
+    row count (1..64, ..128, ..192, ..256 and multi-tile) so each grouped
+    ring configuration runs with many tiles in flight."""
+    counts = [1, 40, 64, 65, 128, 129, 192, 193, 256, 300, 0, 77] * 3
+    N, K = 256, 2048
+    A, Wst, off = _grouped_case(counts, N, K, seed=21)
+    runs = [host(_run_grouped(A, Wst, off)) for _ in range(4)]
+    for r in runs[1:]:
+        assert np.array_equal(r.view(np.uint32), runs[0].view(np.uint32))
+    _check_grouped(torch.from_numpy(runs[0]), A, Wst, off, [1, 3, 8, 9], max_rows=24)
