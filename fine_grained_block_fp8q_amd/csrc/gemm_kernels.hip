@@ -27,13 +27,16 @@
 // into registers before the current chunk's last MFMAs, so the matrix core
 // does not drain at chunk boundaries.  LDS rows are 128 bytes (one K chunk)
 // with the 16-byte column index XOR-swizzled per row so fragment reads are
-// bank-conflict free.
+// bank-conflict free.  The dense kernel's two-stage ring is backed by an L2
+// prefetch several chunks ahead, split between the tiles that share a band
+// of A or W rows in one XCD's L2.
 
 #include "gemm_common.hpp"
 
 namespace fp8q {
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int ROWS_ = BM_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int ROWS_ = BM_,
+          int PF_ = 0>
 struct GemmCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -52,7 +55,9 @@ struct GemmCfg {
   static constexpr int SA_BYTES = NWAVES * 256;     // 64 row scales per wave
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int STAGES = STAGES_;
-  static constexpr int LDS_BYTES = STAGE * STAGES;
+  static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
+  static constexpr int PF_BYTES = PF_LOADS > 0 ? NWAVES * 256 : 0;  // their LDS landing slots
+  static constexpr int LDS_BYTES = STAGE * STAGES + PF_BYTES;
   static constexpr int A_BLK = A_BYTES / 1024;      // 1 KiB load instructions for A
   static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
   static constexpr int PER_WAVE = OP_BLK / NWAVES;  // operand loads per wave per chunk
@@ -62,12 +67,17 @@ struct GemmCfg {
   static_assert(ROWS % 64 == 0 && ROWS <= BM, "staged rows cover whole waves");
   static_assert(OP_BLK % NWAVES == 0, "tile loads must split evenly over the waves");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert(STAGES >= 2 && STAGES <= 6 && LOADS * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(STAGES >= 2 && STAGES <= 6, "ring depth");
+  static_assert(PF_LOADS == 0 || (PF_LOADS == 1 && NWAVES >= 2 && ROWS == 256 && BN == 256),
+                "the prefetch share is laid out for 256 x 256 tiles");
+  static_assert(LOADS * (STAGES - 1) + PF_LOADS * (STAGES - 1) < 64, "vmcnt range");
 };
 
 // Dense configuration: 256 x 256 tiles, 8 waves (two per SIMD, so one wave's
-// promotion FMAs overlap the other's MFMAs), 2 stages (132 KiB of LDS).
-using DenseCfg = GemmCfg<256, 256, 4, 2, 2>;
+// promotion FMAs overlap the other's MFMAs), 2 stages (132 KiB of LDS) and an
+// L2 prefetch kPfDist chunks ahead (a ring of 2 stages leaves the loads of a
+// chunk less than one chunk's compute time to arrive from HBM).
+using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 // Grouped configurations: 256-row tiles cover an expert's tokens (decode
 // batches hold at most 256) so each expert's weights stream once per n-tile.
 // Only the tile's live rows (rounded up to 64) are staged, and the LDS this
@@ -87,6 +97,9 @@ using GroupedCfg = GemmCfg<256, 128, 4, 2, S, ROWS>;
 //   kBPrefetch       weight fragments are read this many row blocks ahead;
 //   kBarLead         the chunk barrier sits this many MFMAs before the
 //                    chunk's last row block.
+//   kPfDist          the L2 prefetch issued while chunk g is computed
+//                    touches chunk g + kPfDist.
+constexpr int kPfDist = 6;
 constexpr int kDma0 = 1;
 constexpr int kDmaStep = 2;
 constexpr int kPromoteLag = 2;
@@ -110,6 +123,8 @@ struct ChunkLoader {
   __amdgpu_buffer_rsrc_t ra, rw, rs;
   uint32_t voff[Cfg::PER_WAVE];
   uint32_t voff_s;
+  uint32_t voff_pf;  // this lane's L2 prefetch line (first byte of its K chunk)
+  bool pf_a;         // the wave prefetches A rows (else W rows)
   int64_t s_stride;  // bytes between consecutive chunks' row scales
   int wave;
 
@@ -138,6 +153,27 @@ struct ChunkLoader {
     // 32 + c, 48 + c) sit side by side in LDS.
     const int64_t rs_row = wave_m * 64 + (lane & 3) * 16 + (lane >> 2);
     voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
+    // L2 prefetch lines.  The XCD-aware tile order gives one XCD a block of
+    // 4 tile rows x 8 tile columns, so 8 tiles share each 256-row A band and
+    // 4 share each W band in that XCD's L2.  A tile therefore prefetches
+    // only its share: A rows 32*(tn%8) .. +31 (wave 0, lanes 0..31) and W
+    // rows 64*(tm%4) .. +63 (wave 1).  Every other lane repeats its wave's
+    // first line, which the address unit merges into one request: a prefetch
+    // costs 96 line requests per tile and chunk instead of 512.
+    const int tm = (int)(t.a_row0 / Cfg::BM), tn = (int)(t.w_row0 / Cfg::BN);
+    pf_a = wave != 1;
+    int pr = pf_a ? 32 * (tn % 8) : 64 * (tm % 4);
+    if (wave == 1 || (wave == 0 && lane < 32)) pr += lane;
+    const int64_t plive = pf_a ? a_live : w_live;
+    voff_pf = (uint32_t)((pr < plive ? pr : plive - 1) * t.K);
+  }
+
+  // L2 prefetch h (0 .. PF_LOADS-1) of this lane's line of chunk g: a 4-byte
+  // direct-to-LDS load into the wave's landing slot, whose contents nobody
+  // reads.  It is counted by vmcnt like the operand loads.
+  __device__ __forceinline__ void prefetch(uint8_t* slot, int64_t g, int h) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pf_a ? ra : rw, to_lds(slot), 4,
+                                             voff_pf + (uint32_t)(h * 64), (int)(g * Cfg::BK), 0, 0);
   }
 
   // Load d (0 .. LOADS-1) of chunk g into `stage`.
@@ -229,6 +265,11 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   };
   static_assert(kDma0 + (Cfg::LOADS - D1 - 1) * kDmaStep < kBar,
                 "head loads are issued before the barrier");
+  // The prefetches follow the head loads, kDmaStep MFMAs apart.
+  constexpr int kPfAt = kDma0 + (Cfg::LOADS - D1) * kDmaStep;
+  static_assert(kPfAt > kDma0 + (Cfg::LOADS - D1 - 1) * kDmaStep &&
+                    kPfAt + (Cfg::PF_LOADS - 1) * kDmaStep < kBar,
+                "prefetches go out after the head loads and before the barrier");
 
   ChunkLoader<Cfg> ld;
   ld.init(t, wave, wave_m, lane);
@@ -236,15 +277,28 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   // re-fetch L2-resident bytes into a stage nobody reads again, and keep the
   // number of loads in flight the same every iteration.
   const int64_t g_last = G - 1;
+  uint8_t* const pf_slot = smem + S * Cfg::STAGE + wave * 256;
+  constexpr int PFL = Cfg::PF_LOADS;
+  // Loads issued after the last load of the chunk a barrier waits for: in
+  // steady state S-2 whole chunks and S-1 iterations' prefetches.
+  constexpr int kAfter = Cfg::LOADS * (S - 2) + PFL * (S - 1);
+  // The prologue issues chunks 0 .. S-2 and the first D1 loads of chunk S-1
+  // in the order S-1 steady-state iterations would (each chunk followed by
+  // one iteration's prefetches), so every wait below counts the same loads.
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
+  for (int s = 0; s < S - 1; ++s) {
 #pragma unroll
     for (int d = 0; d < Cfg::LOADS; ++d)
       ld.issue(smem + s * Cfg::STAGE, s < g_last ? s : g_last, d);
+    const int64_t gp = s - (S - 1) + kPfDist;
+#pragma unroll
+    for (int h = 0; h < PFL; ++h)
+      ld.prefetch(pf_slot, gp < 0 ? 0 : (gp < g_last ? gp : g_last), h);
+  }
 #pragma unroll
   for (int d = 0; d < D1; ++d)
     ld.issue(smem + (S - 1) * Cfg::STAGE, S - 1 < g_last ? S - 1 : g_last, d);
-  wait_vmcnt<Cfg::LOADS * (S - 2) + D1>();  // chunk 0 landed
+  wait_vmcnt<kAfter + D1>();  // chunk 0 landed
   lds_barrier();
 
   v8i a[MB];     // activation fragments of the chunk (MFMA B operand)
@@ -263,13 +317,16 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
     const int head = cur == 0 ? S - 1 : cur - 1;   // stage of chunk g+S-1
     const int64_t g_head = g + S - 1 < g_last ? g + S - 1 : g_last;
     const int64_t g_tail = g + S < g_last ? g + S : g_last;
+    const int64_t g_pf = g + kPfDist < g_last ? g + kPfDist : g_last;
     uint8_t* const st_cur = smem + cur * Cfg::STAGE;
     uint8_t* const st_nxt = smem + nxt * Cfg::STAGE;
     uint8_t* const st_head = smem + head * Cfg::STAGE;
     if (!wave_live) {
 #pragma unroll
       for (int d = D1; d < Cfg::LOADS; ++d) ld.issue(st_head, g_head, d);
-      wait_vmcnt<Cfg::LOADS * (S - 2)>();
+#pragma unroll
+      for (int h = 0; h < PFL; ++h) ld.prefetch(pf_slot, g_pf, h);
+      wait_vmcnt<kAfter>();
       lds_barrier();
 #pragma unroll
       for (int d = 0; d < D1; ++d) ld.issue(st_cur, g_tail, d);
@@ -298,8 +355,11 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
 #pragma unroll
       for (int d = D1; d < Cfg::LOADS; ++d)
         if (k == kDma0 + (d - D1) * kDmaStep) ld.issue(st_head, g_head, d);
+#pragma unroll
+      for (int h = 0; h < PFL; ++h)
+        if (k == kPfAt + h * kDmaStep) ld.prefetch(pf_slot, g_pf, h);
       if (k == kBar) {
-        wait_vmcnt<Cfg::LOADS * (S - 2)>();  // chunk g+1 landed
+        wait_vmcnt<kAfter>();  // chunk g+1 landed
         lds_barrier();
       }
       if (k < MB * NB) {
