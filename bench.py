@@ -284,7 +284,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     # Per-kernel durations: HIP events on the launch stream around `steps`
-    # back-to-back launches of each kernel (same inputs, same launch shape).
+    # back-to-back launches of each kernel (same inputs, same launch shape);
+    # then the same launches once more, each with its own event pair, for the
+    # median and the 10th / 90th percentiles.
     kout = {}
     for kname, bound, work, unit in kernels:
         e0 = torch.cuda.Event(enable_timing=True)
@@ -295,14 +297,25 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         avg_ms = e0.elapsed_time(e1) / args.steps
+        # Spread: one event pair per launch (the same launches again).
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+        for i, (a, b) in enumerate(pairs):
+            a.record()
+            launch(kname, args.warmup + i)
+            b.record()
+        torch.cuda.synchronize()
+        each = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+        spread = {"median_us": float(np.median(each)), "p10_us": float(np.percentile(each, 10)),
+                  "p90_us": float(np.percentile(each, 90))}
         if unit == "B":
             ach = work / (avg_ms * 1e-3) / 1e9
             kout[kname] = {"avg_us": avg_ms * 1e3, "GB_s": ach, "frac_hbm": ach / PEAK_HBM_GBS,
-                           "bytes": work}
+                           "bytes": work, **spread}
         else:
             ach = work / (avg_ms * 1e-3) / 1e12
             kout[kname] = {"avg_us": avg_ms * 1e3, "TFLOP_s": ach,
-                           "frac_fp8_peak": ach / PEAK_FP8_TFLOPS, "flops": work}
+                           "frac_fp8_peak": ach / PEAK_FP8_TFLOPS, "flops": work, **spread}
 
     if args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm"]
