@@ -215,3 +215,60 @@ def test_grouped_determinism_all_tile_configs():
     for r in runs[1:]:
         assert np.array_equal(r.view(np.uint32), runs[0].view(np.uint32))
     _check_grouped(torch.from_numpy(runs[0]), A, Wst, off, [1, 3, 8, 9], max_rows=24)
+
+
+def test_grouped_moe_workload_sampled():
+    """MoE shape at full size: 4096 tokens routed top-8 over 256 experts
+    (32768 gathered rows), N 4096, K 7168, FP32 out, in the launch bench.py
+    times.  Weights are drawn on the device and quantized expert by expert;
+    the oracle checks the codes of 4 sampled experts bit-exactly and their
+    GEMM outputs on sampled rows, plus the activation codes of those rows."""
+    cfg = workloads.WORKLOADS["moe"]
+    G, N, K = cfg["experts"], cfg["N"], cfg["K"]
+    counts, off, token_of = workloads.moe_routing(cfg["tokens"], G, cfg["topk"], cfg["seed"])
+    assert int(off[-1]) == cfg["tokens"] * cfg["topk"]
+    outl = workloads.outlier_channels(K, cfg["seed"], cfg["outlier_frac"], cfg["outlier_count"])
+    tok = workloads.rows_threaded(workloads.act_rows, np.arange(cfg["tokens"]), K, cfg["seed"],
+                                  cfg["act_std"], outl, cfg["outlier_mult"])
+    A = tok[token_of]
+    f = fq()
+    wq = torch.empty((G, N, K), dtype=torch.uint8, device=DEV)
+    ws = torch.empty((G, N // 128, K // 128), dtype=torch.float32, device=DEV)
+    for e in range(G):
+        f.fp8q_quantize_weight(workloads.expert_weight_torch(e, N, K, cfg["seed"], cfg["w_std"],
+                                                             DEV), wq[e], ws[e])
+    aq, as_ = f.quantize_act(to_dev_bf16(A))
+    c = torch.full((A.shape[0], N), float("nan"), dtype=torch.float32, device=DEV)
+    f.fp8q_grouped_gemm(aq, as_, torch.from_numpy(off).to(DEV), wq, ws, c)
+    torch.cuda.synchronize()
+    for e in (0, int(np.argmin(counts)), int(np.argmax(counts)), G - 1):
+        Wb = bf16_to_bits(workloads.expert_weight_torch(e, N, K, cfg["seed"], cfg["w_std"], DEV))
+        qw, sw = oquant.quantize_weight(Wb)
+        assert np.array_equal(host(wq[e]), qw), f"expert {e} weight codes"
+        assert np.array_equal(host(ws[e]).view(np.uint32), sw.view(np.uint32))
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows = np.arange(r0, r1)
+        rows = np.sort(np.random.default_rng(e).choice(rows, min(16, len(rows)), replace=False))
+        # quantization is row-wise, so the sampled rows quantize on their own
+        qa, sa = oquant.quantize_act(A[rows])
+        assert np.array_equal(host(aq[torch.from_numpy(rows).to(DEV)]), qa)
+        assert np.array_equal(host(as_[:, torch.from_numpy(rows).to(DEV)]).view(np.uint32),
+                              sa.view(np.uint32))
+        ch = host(c[torch.from_numpy(rows).to(DEV)])
+        assert_gemm_close(ch, qa, sa, qw, sw, model_rows=2, what=f"moe expert {e}")
+
+
+@pytest.mark.parametrize("G", [1000, 1024])
+def test_grouped_many_experts(G):
+    """Up to the 1024-expert limit: the device prefix scan runs over two
+    512-expert chunks.  Most experts are empty; the others hold 1..70 rows,
+    including the first and the last expert."""
+    rng = np.random.default_rng(G)
+    counts = np.where(rng.random(G) < 0.08, rng.integers(1, 71, G), 0)
+    counts[0], counts[-1], counts[511], counts[512] = 3, 65, 1, 64
+    N, K = 128, 256
+    A, Wst, off = _grouped_case(list(counts), N, K, seed=G, extra_rows=3)
+    c = _run_grouped(A, Wst, off)
+    live = [e for e in range(G) if counts[e] > 0]
+    _check_grouped(c, A, Wst, off, live)
+    assert np.all(np.isnan(_c_host(c)[off[-1]:])), "rows past off[G] must be left untouched"
