@@ -18,8 +18,8 @@
 // matrix core runs the next MFMAs (the role the pages give to two alternating
 // warpgroups on Hopper).
 //
-// Each wave owns 64 activation rows and 128 (dense) or 64 (grouped) weight
-// rows inside one 128-row weight block, so s_w is one wave-uniform scalar per
+// Each wave owns 64 activation rows and 128 weight rows inside one 128-row
+// weight block, so s_w is one wave-uniform scalar per
 // chunk, and the 64 row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
 // LDS with 16-byte direct-to-LDS buffer loads (no VGPR staging) through a ring
 // of STAGES K chunks with one barrier per chunk; the loads of the chunks ahead
@@ -79,14 +79,17 @@ struct GemmCfg {
 // chunk less than one chunk's compute time to arrive from HBM).
 using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 // Grouped configurations: 256-row tiles cover an expert's tokens (decode
-// batches hold at most 256) so each expert's weights stream once per n-tile.
+// batches hold at most 256) so each expert's weights stream once, and 256
+// weight rows per tile (8 waves of 64 x 128, as in the dense tile) so each
+// expert's activation rows are re-read from L2 by N/256 tiles rather than
+// N/128 (at 128 weight rows the activation reads outweighed the weight
+// stream in large tiles and held the weight stream below the copy rate).
 // Only the tile's live rows (rounded up to 64) are staged, and the LDS this
-// frees deepens the ring: 6 / 4 / 3 / 3 stages for 64 / 128 / 192 / 256 rows,
-// i.e. up to 80 KiB of weights in flight per CU.  8 waves of 64 x 64 (two
-// per SIMD) rather than 4 of 64 x 128: a tile with few live rows still keeps
-// every SIMD busy, and each SIMD has a second wave to cover its stalls.
+// frees deepens the ring: 3 / 3 / 2 / 2 stages for 64 / 128 / 192 / 256 rows.
+constexpr int kGroupedBN = 256;
 template <int ROWS, int S>
-using GroupedCfg = GemmCfg<256, 128, 4, 2, S, ROWS>;
+using GroupedCfg = GemmCfg<256, kGroupedBN, 4, 2, S, ROWS>;
+constexpr int kS64 = 3, kS128 = 3, kS192 = 2, kS256 = 2;
 
 // Main-loop schedule constants (measured on the 4096 x 4096 x 7168 shape;
 // the result is insensitive to them within +-2%):
@@ -448,14 +451,16 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
 constexpr int kMaxExpertsLds = 1024;
 constexpr int kGroupedThreads = 512;
 constexpr int kGroupedLds =
-    GroupedCfg<64, 6>::LDS_BYTES > GroupedCfg<128, 4>::LDS_BYTES
-        ? (GroupedCfg<64, 6>::LDS_BYTES > GroupedCfg<256, 3>::LDS_BYTES
-               ? GroupedCfg<64, 6>::LDS_BYTES
-               : GroupedCfg<256, 3>::LDS_BYTES)
-        : GroupedCfg<128, 4>::LDS_BYTES;
-static_assert(GroupedCfg<192, 3>::LDS_BYTES <= kGroupedLds, "grouped LDS sizing");
-static_assert(GroupedCfg<64, 6>::THREADS == kGroupedThreads &&
-                  GroupedCfg<256, 3>::THREADS == kGroupedThreads,
+    GroupedCfg<64, kS64>::LDS_BYTES > GroupedCfg<128, kS128>::LDS_BYTES
+        ? (GroupedCfg<64, kS64>::LDS_BYTES > GroupedCfg<256, kS256>::LDS_BYTES
+               ? GroupedCfg<64, kS64>::LDS_BYTES
+               : GroupedCfg<256, kS256>::LDS_BYTES)
+        : (GroupedCfg<128, kS128>::LDS_BYTES > GroupedCfg<256, kS256>::LDS_BYTES
+               ? GroupedCfg<128, kS128>::LDS_BYTES
+               : GroupedCfg<256, kS256>::LDS_BYTES);
+static_assert(GroupedCfg<192, kS192>::LDS_BYTES <= kGroupedLds, "grouped LDS sizing");
+static_assert(GroupedCfg<64, kS64>::THREADS == kGroupedThreads &&
+                  GroupedCfg<256, kS256>::THREADS == kGroupedThreads,
               "all grouped configurations use the same workgroup");
 
 __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
@@ -523,7 +528,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   t.SW = SW + (int64_t)e * (N / 128) * (K / 128);
   t.a_row0 = r0 + (int64_t)mt * BM;
   t.a_rows = r1;
-  t.w_row0 = (int64_t)tn * 128;
+  t.w_row0 = (int64_t)tn * kGroupedBN;
   t.w_rows = N;
   t.K = K;
   t.sa_ld = M_total;
@@ -532,13 +537,13 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   t.out_bf16 = out_bf16;
   const int64_t live = r1 - t.a_row0;  // 1 .. (>= 256 when more m-tiles follow)
   if (live <= 64)
-    gemm_tile<GroupedCfg<64, 6>>(t, smem);
+    gemm_tile<GroupedCfg<64, kS64>>(t, smem);
   else if (live <= 128)
-    gemm_tile<GroupedCfg<128, 4>>(t, smem);
+    gemm_tile<GroupedCfg<128, kS128>>(t, smem);
   else if (live <= 192)
-    gemm_tile<GroupedCfg<192, 3>>(t, smem);
+    gemm_tile<GroupedCfg<192, kS192>>(t, smem);
   else
-    gemm_tile<GroupedCfg<256, 3>>(t, smem);
+    gemm_tile<GroupedCfg<256, kS256>>(t, smem);
 }
 
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
@@ -561,7 +566,7 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
                                hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
   if (G > kMaxExpertsLds) return hipErrorInvalidValue;
-  const int64_t tiles_n = (N + 127) / 128;
+  const int64_t tiles_n = (N + kGroupedBN - 1) / kGroupedBN;
   // sum_e ceil(M_e / 256) <= floor(M_total / 256) + G
   const int64_t max_mtiles = M_total / 256 + G;
   const int64_t tiles = max_mtiles * tiles_n;
