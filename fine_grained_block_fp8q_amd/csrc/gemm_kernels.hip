@@ -442,12 +442,28 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
 }
 
 // Grouped variant.  The grid over-provisions tiles; each workgroup maps its id
-// to (expert, m-tile, n-tile) by a prefix sum of ceil(M_e / 256) over the device
-// offsets, held in LDS.  Workgroups past the last real tile exit.  Real tiles
-// are numbered (expert, m-tile)-major, n-tile fastest, and handed to XCDs in
-// contiguous runs (workgroup id mod 8 is its XCD), so the n-tiles of one
-// expert share that expert's rows of A in one L2.  Each tile then runs the
-// instantiation for its live row count.
+// to (expert, m-tile, n-tile) from the device offsets, in LDS: it ranks the
+// experts by row count, orders them for a balanced, largest-first schedule
+// (snake_position), and takes a prefix sum of ceil(M_e / 256) in that order.
+// Workgroups past the last real tile exit.  Real tiles are numbered in that
+// expert order, m-tile, then n-tile fastest, and handed to XCDs in contiguous
+// runs (workgroup id mod 8 is its XCD), so the n-tiles of one expert share
+// that expert's rows of A in one L2.  Each tile then runs the instantiation
+// for its live row count.
+// Position of the expert of rank r (0 = most rows) among G experts dealt to
+// the 8 XCD runs in snake order: ranks 0..7 go to runs 0..7, ranks 8..15 to
+// runs 7..0, and so on; run b holds its experts in rank order, and the runs
+// follow each other.  A bijection on [0, G).
+__device__ __forceinline__ int snake_position(int r, int G) {
+  const int round = r / kXcds, i = r % kXcds;
+  const int bin = (round & 1) ? kXcds - 1 - i : i;
+  const int full = G / kXcds, m = G % kXcds;
+  const bool last_odd = (full & 1) != 0;  // direction of the partial last round
+  int start = bin * full;
+  for (int b = 0; b < bin; ++b) start += (m > 0 && (last_odd ? b >= kXcds - m : b < m)) ? 1 : 0;
+  return start + round;
+}
+
 constexpr int kMaxExpertsLds = 1024;
 constexpr int kGroupedThreads = 512;
 constexpr int kGroupedLds =
@@ -467,24 +483,63 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, int64_t M_total,
     const int32_t* __restrict__ off, int G, const uint8_t* __restrict__ W,
     const float* __restrict__ SW, int64_t N, int64_t K, void* __restrict__ C, int out_bf16,
-    int tiles_n) {
+    int tiles_n, int lpt_max_tiles) {
   constexpr int T = kGroupedThreads;
   constexpr int BM = 256;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGroupedLds];
-  static_assert((kMaxExpertsLds + 1 + T) * 4 <= kGroupedLds, "prefix scratch fits in LDS");
+  static_assert((3 * kMaxExpertsLds + 2 + T) * 4 <= kGroupedLds, "prefix scratch fits in LDS");
   int* mt_prefix = reinterpret_cast<int*>(smem);  // [G + 1], reused before the mainloop
   int* scan = mt_prefix + kMaxExpertsLds + 1;     // [T]
+  int* rows_of = scan + T;                        // [G] rows of expert e
+  int* expert_at = rows_of + kMaxExpertsLds;      // [G] expert at tile-order position p
+  int* total_mt = expert_at + kMaxExpertsLds;     // [1] m-tiles over all experts
 
-  // Prefix over experts of the number of BM-row tiles (chunks of T experts,
-  // each with a Hillis-Steele block scan).
   const int tid = threadIdx.x;
+  if (tid == 0) *total_mt = 0;
+  __syncthreads();
+  int my_mt = 0;
+  for (int e = tid; e < G; e += T) {
+    const int rows = off[e + 1] - off[e];
+    rows_of[e] = rows;
+    my_mt += rows > 0 ? (rows + BM - 1) / BM : 0;
+  }
+  if (my_mt) atomicAdd(total_mt, my_mt);
+  __syncthreads();
+  // Tile order.  When the tiles fill only a few rounds of the chip
+  // (lpt_max_tiles = 4 per CU), the tail of the last round decides the time:
+  // experts ranked by row count (largest first, ties by index) are dealt to
+  // the 8 XCD runs in snake order, and each run lists its experts largest
+  // first, so every XCD gets a similar share of the rows and its CUs take the
+  // largest tiles first.  With many rounds, the expert order is kept: it mixes
+  // tiles of different row counts (different MFMA-to-HBM ratios) in time.
+  // Either way, each expert's tiles stay in one XCD run and share its L2
+  // (exactly so when the runs hold equal tile counts, as with one m-tile per
+  // expert).
+  const bool lpt = *total_mt * tiles_n <= lpt_max_tiles;
+  for (int e = tid; e < G; e += T) {
+    int p = e;
+    if (lpt) {
+      const int ce = rows_of[e];
+      int r = 0;
+      for (int j = 0; j < G; ++j) {
+        const int cj = rows_of[j];
+        r += (cj > ce || (cj == ce && j < e)) ? 1 : 0;
+      }
+      p = snake_position(r, G);
+    }
+    expert_at[p] = e;
+  }
+  __syncthreads();
+
+  // Prefix over tile-order positions of the number of BM-row tiles (chunks of
+  // T positions, each with a Hillis-Steele block scan).
   int running = 0;
   if (tid == 0) mt_prefix[0] = 0;
   for (int base = 0; base < G; base += T) {
-    const int e = base + tid;
+    const int p = base + tid;
     int cnt = 0;
-    if (e < G) {
-      const int rows = off[e + 1] - off[e];
+    if (p < G) {
+      const int rows = rows_of[expert_at[p]];
       cnt = rows > 0 ? (rows + BM - 1) / BM : 0;
     }
     scan[tid] = cnt;
@@ -495,7 +550,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
       scan[tid] += add;
       __syncthreads();
     }
-    if (e < G) mt_prefix[e + 1] = running + scan[tid];
+    if (p < G) mt_prefix[p + 1] = running + scan[tid];
     running += scan[T - 1];
     __syncthreads();
   }
@@ -509,14 +564,14 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   const int id = x * q8 + (x < r8 ? x : r8) + bid / kXcds;
   const int mt_global = id / tiles_n;
   const int tn = id % tiles_n;
-  // expert e with prefix[e] <= mt_global < prefix[e+1]
+  // position p with prefix[p] <= mt_global < prefix[p+1]
   int lo = 0, hi = G;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (mt_prefix[mid] <= mt_global) lo = mid; else hi = mid;
   }
-  const int e = lo;
-  const int mt = mt_global - mt_prefix[e];
+  const int e = expert_at[lo];
+  const int mt = mt_global - mt_prefix[lo];
   const int64_t r0 = off[e];
   const int64_t r1 = off[e + 1];
   __syncthreads();  // mt_prefix is overwritten by the mainloop
@@ -571,9 +626,14 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
   const int64_t max_mtiles = M_total / 256 + G;
   const int64_t tiles = max_mtiles * tiles_n;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // The largest-first order applies up to 4 tiles per CU of the device.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
   hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)tiles), dim3(kGroupedThreads), 0,
                      stream, a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16,
-                     (int)tiles_n);
+                     (int)tiles_n, 4 * cus);
   return hipGetLastError();
 }
 
