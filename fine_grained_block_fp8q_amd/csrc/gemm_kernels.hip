@@ -18,9 +18,9 @@
 // matrix core runs the next MFMAs (the role the pages give to two alternating
 // warpgroups on Hopper).
 //
-// Each wave owns 64 activation rows and 128 weight rows inside one 128-row
-// weight block, so s_w is one wave-uniform scalar per
-// chunk, and the 64 row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
+// Each wave owns 64 (48 in the grouped 192-row tiles) activation rows and 128
+// weight rows inside one 128-row weight block, so s_w is one wave-uniform
+// scalar per chunk, and the row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
 // LDS with 16-byte direct-to-LDS buffer loads (no VGPR staging) through a ring
 // of STAGES K chunks with one barrier per chunk; the loads of the chunks ahead
 // are spread over the MFMA sequence, and the next chunk's fragments are read
@@ -52,7 +52,7 @@ struct GemmCfg {
   static constexpr int ROWS = ROWS_;                // A rows staged per chunk (<= BM)
   static constexpr int A_BYTES = ROWS * BK;
   static constexpr int B_BYTES = BN * BK;
-  static constexpr int SA_BYTES = NWAVES * 256;     // 64 row scales per wave
+  static constexpr int SA_BYTES = NWAVES * 256;     // up to 64 row scales per wave
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
@@ -62,7 +62,7 @@ struct GemmCfg {
   static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
   static constexpr int PER_WAVE = OP_BLK / NWAVES;  // operand loads per wave per chunk
   static constexpr int LOADS = PER_WAVE + 1;        // + the scale slot
-  static_assert(WM == 64, "a wave's rows are 64 (one 256-byte scale slot)");
+  static_assert(WM % 16 == 0 && WM <= 64, "a wave's rows fit one 256-byte scale slot");
   static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
   static_assert(ROWS % 64 == 0 && ROWS <= BM, "staged rows cover whole waves");
   static_assert(OP_BLK % NWAVES == 0, "tile loads must split evenly over the waves");
@@ -87,8 +87,11 @@ using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 // Only the tile's live rows (rounded up to 64) are staged, and the LDS this
 // frees deepens the ring: 3 / 3 / 2 / 2 stages for 64 / 128 / 192 / 256 rows.
 constexpr int kGroupedBN = 256;
+// 192-row tiles hold experts of 129..192 rows: their waves take 48 rows each,
+// so for up to 144 rows the fourth row of waves has none and skips its MFMAs
+// (64-row waves would run three full waves for 129 rows).
 template <int ROWS, int S>
-using GroupedCfg = GemmCfg<256, kGroupedBN, 4, 2, S, ROWS>;
+using GroupedCfg = GemmCfg<(ROWS == 192 ? 192 : 256), kGroupedBN, 4, 2, S, ROWS>;
 constexpr int kS64 = 3, kS128 = 3, kS192 = 2, kS256 = 2;
 
 // Main-loop schedule constants (measured on the 4096 x 4096 x 7168 shape;
@@ -152,9 +155,10 @@ struct ChunkLoader {
       voff[j] = (uint32_t)(rr * t.K) + (uint32_t)(swz(r, pc) * 16);
     }
     // Lane i of the scale load fetches row (i & 3) * 16 + i / 4 of the wave's
-    // 64 rows, so the four scales an MFMA column lane needs (rows c, 16 + c,
-    // 32 + c, 48 + c) sit side by side in LDS.
-    const int64_t rs_row = wave_m * 64 + (lane & 3) * 16 + (lane >> 2);
+    // rows (up to 64; rows past them are loaded and not used), so the scales
+    // an MFMA column lane needs (rows c, 16 + c, 32 + c, 48 + c) sit side by
+    // side in LDS.
+    const int64_t rs_row = wave_m * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
     voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
     // L2 prefetch lines.  The XCD-aware tile order gives one XCD a block of
     // 4 tile rows x 8 tile columns, so 8 tiles share each 256-row A band and
