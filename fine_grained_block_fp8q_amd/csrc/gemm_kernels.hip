@@ -52,7 +52,7 @@ struct GemmCfg {
   static constexpr int ROWS = ROWS_;                // A rows staged per chunk (<= BM)
   static constexpr int A_BYTES = ROWS * BK;
   static constexpr int B_BYTES = BN * BK;
-  static constexpr int SA_BYTES = NWAVES * 256;     // up to 64 row scales per wave
+  static constexpr int SA_BYTES = WAVES_M * 256;    // up to 64 row scales per row of waves
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
@@ -60,12 +60,16 @@ struct GemmCfg {
   static constexpr int LDS_BYTES = STAGE * STAGES + PF_BYTES;
   static constexpr int A_BLK = A_BYTES / 1024;      // 1 KiB load instructions for A
   static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
-  static constexpr int PER_WAVE = OP_BLK / NWAVES;  // operand loads per wave per chunk
+  static constexpr int PER_WAVE = (OP_BLK + NWAVES - 1) / NWAVES;  // operand loads per wave
+  static constexpr int PAD = PER_WAVE * NWAVES - OP_BLK;  // repeated A loads that even them out
   static constexpr int LOADS = PER_WAVE + 1;        // + the scale slot
   static_assert(WM % 16 == 0 && WM <= 64, "a wave's rows fit one 256-byte scale slot");
   static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
-  static_assert(ROWS % 64 == 0 && ROWS <= BM, "staged rows cover whole waves");
-  static_assert(OP_BLK % NWAVES == 0, "tile loads must split evenly over the waves");
+  // Staged rows: whole 1 KiB loads.  When they stop inside a wave (160 rows
+  // in 48-row waves), that wave's fragment reads past them fall inside the
+  // stage and feed only rows past the expert's end, which are not stored.
+  static_assert(ROWS % 32 == 0 && ROWS <= BM, "staged rows fill whole loads within the tile");
+  static_assert(PAD <= A_BLK, "the padding loads repeat A loads");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && STAGES <= 6, "ring depth");
   static_assert(PF_LOADS == 0 || (PF_LOADS == 1 && NWAVES >= 2 && ROWS == 256 && BN == 256),
@@ -84,15 +88,20 @@ using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 // expert's activation rows are re-read from L2 by N/256 tiles rather than
 // N/128 (at 128 weight rows the activation reads outweighed the weight
 // stream in large tiles and held the weight stream below the copy rate).
-// Only the tile's live rows (rounded up to 64) are staged, and the LDS this
-// frees deepens the ring: 3 / 3 / 2 / 2 stages for 64 / 128 / 192 / 256 rows.
+// Only the tile's live rows are staged (64, 128, 160, 192 or 256), and the
+// LDS this frees deepens the ring: 3 stages up to 160 rows, 2 above.  A
+// 2-stage ring streams the weights markedly slower than a 3-stage one once
+// the activation rows share the loads, so 160 rows (most experts of a
+// 256-expert top-8 routing of 4096 tokens hold 103..157) get a bucket of
+// their own: the largest that still fits 3 stages in 160 KiB.
 constexpr int kGroupedBN = 256;
-// 192-row tiles hold experts of 129..192 rows: their waves take 48 rows each,
-// so for up to 144 rows the fourth row of waves has none and skips its MFMAs
-// (64-row waves would run three full waves for 129 rows).
+// 160- and 192-row tiles hold experts of 129..192 rows: their waves take 48
+// rows each, so for up to 144 rows the fourth row of waves has none and
+// skips its MFMAs (64-row waves would run three full waves for 129 rows).
 template <int ROWS, int S>
-using GroupedCfg = GemmCfg<(ROWS == 192 ? 192 : 256), kGroupedBN, 4, 2, S, ROWS>;
-constexpr int kS64 = 3, kS128 = 3, kS192 = 2, kS256 = 2;
+using GroupedCfg =
+    GemmCfg<(ROWS == 160 || ROWS == 192 ? 192 : 256), kGroupedBN, 4, 2, S, ROWS>;
+constexpr int kS64 = 3, kS128 = 3, kS160 = 3, kS192 = 2, kS256 = 2;
 
 // Main-loop schedule constants (measured on the 4096 x 4096 x 7168 shape;
 // the result is insensitive to them within +-2%):
@@ -114,9 +123,12 @@ constexpr int kBarLead = 2;
 
 // Direct-to-LDS loads of one K chunk (A rows, W rows, row scales).  The
 // operand tiles are cut into 1 KiB load instructions (8 rows of 128 B):
-// instructions 0 .. A_BLK-1 carry A rows, the rest W rows, and wave w issues
-// instructions w*PER_WAVE .. w*PER_WAVE + PER_WAVE - 1, then one 256-byte
-// slot of its 64 row scales: Cfg::LOADS instructions per wave per chunk.  Lane
+// instructions 0 .. A_BLK-1 carry A rows, the next ones W rows, and wave w
+// issues instructions w*PER_WAVE .. w*PER_WAVE + PER_WAVE - 1, then the
+// 256-byte slot of its row of waves' row scales (both waves of a row write
+// the same values there): Cfg::LOADS instructions per wave per chunk.  When
+// the operand loads do not split evenly over the waves, the last PAD
+// instructions repeat the first A loads (same bytes to the same LDS place).  Lane
 // i of an instruction lands at LDS byte 16*i, i.e. row i/8, physical column
 // i%8, and so fetches logical column swz(row, i%8).  Rows past the valid range
 // are clamped to the last valid row (their results are never stored).
@@ -132,10 +144,16 @@ struct ChunkLoader {
   uint32_t voff_pf;  // this lane's L2 prefetch line (first byte of its K chunk)
   bool pf_a;         // the wave prefetches A rows (else W rows)
   int64_t s_stride;  // bytes between consecutive chunks' row scales
-  int wave;
+  int wave, wave_m;
 
-  __device__ __forceinline__ void init(const TileArgs& t, int wave_, int wave_m, int lane) {
+  // Operand block of load instruction m (the padding repeats A blocks).
+  static __device__ __forceinline__ int op_block(int m) {
+    return m < Cfg::OP_BLK ? m : m - Cfg::OP_BLK;
+  }
+
+  __device__ __forceinline__ void init(const TileArgs& t, int wave_, int wave_m_, int lane) {
     wave = wave_;
+    wave_m = wave_m_;
     const int64_t a_live = t.a_rows - t.a_row0;  // >= 1
     const int64_t w_live = t.w_rows - t.w_row0;  // >= 1
     ra = make_rsrc(t.A + t.a_row0 * t.K, a_live * t.K);
@@ -147,7 +165,7 @@ struct ChunkLoader {
     const int pc = lane & 7;
 #pragma unroll
     for (int j = 0; j < Cfg::PER_WAVE; ++j) {
-      const int m = wave * Cfg::PER_WAVE + j;
+      const int m = op_block(wave * Cfg::PER_WAVE + j);
       const bool is_a = m < Cfg::A_BLK;
       const int r = (is_a ? m : m - Cfg::A_BLK) * 8 + sub_r;
       const int64_t live = is_a ? a_live : w_live;
@@ -158,7 +176,7 @@ struct ChunkLoader {
     // rows (up to 64; rows past them are loaded and not used), so the scales
     // an MFMA column lane needs (rows c, 16 + c, 32 + c, 48 + c) sit side by
     // side in LDS.
-    const int64_t rs_row = wave_m * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
+    const int64_t rs_row = wave_m_ * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
     voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
     // L2 prefetch lines.  The XCD-aware tile order gives one XCD a block of
     // 4 tile rows x 8 tile columns, so 8 tiles share each 256-row A band and
@@ -186,14 +204,14 @@ struct ChunkLoader {
   // Load d (0 .. LOADS-1) of chunk g into `stage`.
   __device__ __forceinline__ void issue(uint8_t* stage, int64_t g, int d) const {
     if (d < Cfg::PER_WAVE) {
-      const int m = wave * Cfg::PER_WAVE + d;
+      const int m = op_block(wave * Cfg::PER_WAVE + d);
       const bool is_a = m < Cfg::A_BLK;
       const int dst = is_a ? m * 1024 : Cfg::A_BYTES + (m - Cfg::A_BLK) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rw, to_lds(stage + dst), 16, voff[d],
                                                (int)(g * Cfg::BK), 0, 0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256), 4, voff_s,
+          rs, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256), 4, voff_s,
           (int)(g * s_stride), 0, 0);
     }
   }
@@ -343,7 +361,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
 
     const uint8_t* Bs = st_cur + Cfg::A_BYTES;
     const float* SAs =
-        reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256);
+        reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256);
     const float sw = sw_row[g];
     const v4f sa = *reinterpret_cast<const v4f*>(SAs + 4 * r16);
     float mult[MB];
@@ -468,17 +486,13 @@ __device__ __forceinline__ int snake_position(int r, int G) {
   return start + round;
 }
 
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int kMaxExpertsLds = 1024;
 constexpr int kGroupedThreads = 512;
 constexpr int kGroupedLds =
-    GroupedCfg<64, kS64>::LDS_BYTES > GroupedCfg<128, kS128>::LDS_BYTES
-        ? (GroupedCfg<64, kS64>::LDS_BYTES > GroupedCfg<256, kS256>::LDS_BYTES
-               ? GroupedCfg<64, kS64>::LDS_BYTES
-               : GroupedCfg<256, kS256>::LDS_BYTES)
-        : (GroupedCfg<128, kS128>::LDS_BYTES > GroupedCfg<256, kS256>::LDS_BYTES
-               ? GroupedCfg<128, kS128>::LDS_BYTES
-               : GroupedCfg<256, kS256>::LDS_BYTES);
-static_assert(GroupedCfg<192, kS192>::LDS_BYTES <= kGroupedLds, "grouped LDS sizing");
+    cmax(cmax(GroupedCfg<64, kS64>::LDS_BYTES, GroupedCfg<128, kS128>::LDS_BYTES),
+         cmax(cmax(GroupedCfg<160, kS160>::LDS_BYTES, GroupedCfg<192, kS192>::LDS_BYTES),
+              GroupedCfg<256, kS256>::LDS_BYTES));
 static_assert(GroupedCfg<64, kS64>::THREADS == kGroupedThreads &&
                   GroupedCfg<256, kS256>::THREADS == kGroupedThreads,
               "all grouped configurations use the same workgroup");
@@ -599,6 +613,8 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
     gemm_tile<GroupedCfg<64, kS64>>(t, smem);
   else if (live <= 128)
     gemm_tile<GroupedCfg<128, kS128>>(t, smem);
+  else if (live <= 160)
+    gemm_tile<GroupedCfg<160, kS160>>(t, smem);
   else if (live <= 192)
     gemm_tile<GroupedCfg<192, kS192>>(t, smem);
   else

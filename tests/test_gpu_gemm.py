@@ -206,15 +206,18 @@ def test_grouped_decode_workload_sampled():
 
 def test_grouped_determinism_all_tile_configs():
     """Repeated launches are bitwise identical, with experts of every staged
-    row count (1..64, ..128, ..192, ..256 and multi-tile) so each grouped
-    ring configuration runs with many tiles in flight."""
-    counts = [1, 40, 64, 65, 128, 129, 192, 193, 256, 300, 0, 77] * 3
+    row count (1..64, ..128, ..160, ..192, ..256 and multi-tile) so each
+    grouped ring configuration runs with many tiles in flight.  150 and 160
+    rows put live rows in the fourth row of 48-row waves of a 160-row tile."""
+    counts = [1, 40, 64, 65, 128, 129, 150, 160, 161, 192, 193, 256, 300, 0, 77] * 3
     N, K = 256, 2048
     A, Wst, off = _grouped_case(counts, N, K, seed=21)
     runs = [host(_run_grouped(A, Wst, off)) for _ in range(4)]
     for r in runs[1:]:
         assert np.array_equal(r.view(np.uint32), runs[0].view(np.uint32))
-    _check_grouped(torch.from_numpy(runs[0]), A, Wst, off, [1, 3, 8, 9], max_rows=24)
+    c0 = torch.from_numpy(runs[0])
+    _check_grouped(c0, A, Wst, off, [1, 3, 5, 8, 11, 12], max_rows=24)
+    _check_grouped(c0, A, Wst, off, [6, 7])  # every row of the 150- and 160-row experts
 
 
 def test_grouped_moe_workload_sampled():
