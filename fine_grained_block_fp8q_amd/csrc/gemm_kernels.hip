@@ -18,12 +18,13 @@
 // matrix core runs the next MFMAs (the role the pages give to two alternating
 // warpgroups on Hopper).
 //
-// Each wave owns 64 (48 in the grouped 192-row tiles) activation rows and 128
-// weight rows inside one 128-row weight block, so s_w is one wave-uniform
-// scalar per chunk, and the row scales are one 256-byte LDS slot per chunk.  Operands move HBM/L2 ->
-// LDS with 16-byte direct-to-LDS buffer loads (no VGPR staging) through a ring
-// of STAGES K chunks with one barrier per chunk; the loads of the chunks ahead
-// are spread over the MFMA sequence, and the next chunk's fragments are read
+// Each wave owns 64 (48 in the grouped 160- and 192-row tiles) activation rows
+// and 128 weight rows inside one 128-row weight block, so s_w is one
+// wave-uniform scalar per chunk, and the row scales of a row of waves are one
+// 256-byte LDS slot per chunk.  Operands move HBM/L2 -> LDS with 16-byte
+// direct-to-LDS buffer loads (no VGPR staging) through a ring of STAGES K
+// chunks with one barrier per chunk; the loads of the chunks ahead are spread
+// over the MFMA sequence, and the next chunk's fragments are read
 // into registers before the current chunk's last MFMAs, so the matrix core
 // does not drain at chunk boundaries.  LDS rows are 128 bytes (one K chunk)
 // with the 16-byte column index XOR-swizzled per row so fragment reads are
