@@ -464,15 +464,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
   gemm_tile<Cfg>(t, smem);
 }
 
-// Grouped variant.  The grid over-provisions tiles; each workgroup maps its id
-// to (expert, m-tile, n-tile) from the device offsets, in LDS: it ranks the
-// experts by row count, orders them for a balanced, largest-first schedule
-// (snake_position), and takes a prefix sum of ceil(M_e / 256) in that order.
-// Workgroups past the last real tile exit.  Real tiles are numbered in that
-// expert order, m-tile, then n-tile fastest, and handed to XCDs in contiguous
-// runs (workgroup id mod 8 is its XCD), so the n-tiles of one expert share
-// that expert's rows of A in one L2.  Each tile then runs the instantiation
-// for its live row count.
+// Grouped variant, persistent: one workgroup per CU (the grid grows only if a
+// workgroup would otherwise walk more than 64 tiles).  Each workgroup derives
+// the whole schedule from the device offsets, in LDS, once: it ranks the
+// experts by row count and orders them for a balanced, largest-first
+// schedule (snake_position) when the tiles fill few rounds, takes a prefix
+// sum of ceil(M_e / 256) in that order, and maps each of its own tiles to
+// (expert, m-tile, n-tile), one tile per lane.  It then runs the tiles one
+// after the other, each with the instantiation for its live row count.
+// Paying the set-up once per CU rather than once per tile (a kernel of one
+// workgroup per tile spent about 4 us per workgroup on launch and set-up
+// that the single resident workgroup of a CU cannot overlap).
+
 // Position of the expert of rank r (0 = most rows) among G experts dealt to
 // the 8 XCD runs in snake order: ranks 0..7 go to runs 0..7, ranks 8..15 to
 // runs 7..0, and so on; run b holds its experts in rank order, and the runs
@@ -506,23 +509,39 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   constexpr int T = kGroupedThreads;
   constexpr int BM = 256;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGroupedLds];
-  static_assert((3 * kMaxExpertsLds + 2 + T) * 4 <= kGroupedLds, "prefix scratch fits in LDS");
-  int* mt_prefix = reinterpret_cast<int*>(smem);  // [G + 1], reused before the mainloop
-  int* scan = mt_prefix + kMaxExpertsLds + 1;     // [T]
-  int* rows_of = scan + T;                        // [G] rows of expert e
+  static_assert((3 * kMaxExpertsLds + 1) * 4 <= kGroupedLds, "prefix scratch fits in LDS");
+  static_assert(kMaxExpertsLds % 64 == 0, "one wave scans the experts");
+  int* mt_prefix = reinterpret_cast<int*>(smem);  // [G + 1], reused by the tiles' rings
+  int* rows_of = mt_prefix + kMaxExpertsLds + 1;  // [G] rows of expert e
   int* expert_at = rows_of + kMaxExpertsLds;      // [G] expert at tile-order position p
-  int* total_mt = expert_at + kMaxExpertsLds;     // [1] m-tiles over all experts
+  auto mtiles = [](int rows) { return rows > 0 ? (rows + BM - 1) / BM : 0; };
 
+  // Number of real tiles, computed by every wave on its own from the offsets
+  // (a lane sum and a wave reduction, no barrier), so that workgroups without
+  // a tile leave before any LDS work.
   const int tid = threadIdx.x;
-  if (tid == 0) *total_mt = 0;
-  __syncthreads();
-  int my_mt = 0;
-  for (int e = tid; e < G; e += T) {
-    const int rows = off[e + 1] - off[e];
-    rows_of[e] = rows;
-    my_mt += rows > 0 ? (rows + BM - 1) / BM : 0;
-  }
-  if (my_mt) atomicAdd(total_mt, my_mt);
+  const int lane = tid & 63;
+  int sum_mt = 0;
+  for (int e = lane; e < G; e += 64) sum_mt += mtiles(off[e + 1] - off[e]);
+  for (int d = 32; d >= 1; d >>= 1) sum_mt += __shfl_xor(sum_mt, d);
+  // (equal in every lane; readfirstlane keeps everything derived from it scalar)
+  const int total = __builtin_amdgcn_readfirstlane(sum_mt) * tiles_n;  // real tiles
+  // Persistent schedule.  XCD x (= workgroup id mod 8) takes a contiguous run
+  // of the real tiles, [x*q8 + min(x, r8), ...), so the n-tiles of one expert
+  // share that expert's rows of A in one L2.  The K8 workgroups of an XCD walk
+  // its run in rounds of K8 tiles in snake order (workgroup k takes run
+  // position k in even rounds and K8-1-k in odd ones), which pairs the
+  // largest tiles of a largest-first order with the smallest.  The host sizes
+  // the grid so that no workgroup has more than 64 rounds.
+  const int bid = blockIdx.x;
+  const int K8 = gridDim.x / kXcds;
+  const int x = bid % kXcds, k = bid / kXcds;
+  const int q8 = total / kXcds, r8 = total % kXcds;
+  const int run0 = x * q8 + (x < r8 ? x : r8);
+  const int len = q8 + (x < r8 ? 1 : 0);
+  if (k >= len) return;  // no tile for this workgroup
+
+  for (int e = tid; e < G; e += T) rows_of[e] = off[e + 1] - off[e];
   __syncthreads();
   // Tile order.  When the tiles fill only a few rounds of the chip
   // (lpt_max_tiles = 4 per CU), the tail of the last round decides the time:
@@ -534,7 +553,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   // Either way, each expert's tiles stay in one XCD run and share its L2
   // (exactly so when the runs hold equal tile counts, as with one m-tile per
   // expert).
-  const bool lpt = *total_mt * tiles_n <= lpt_max_tiles;
+  const bool lpt = total <= lpt_max_tiles;
   for (int e = tid; e < G; e += T) {
     int p = e;
     if (lpt) {
@@ -550,76 +569,85 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   }
   __syncthreads();
 
-  // Prefix over tile-order positions of the number of BM-row tiles (chunks of
-  // T positions, each with a Hillis-Steele block scan).
-  int running = 0;
-  if (tid == 0) mt_prefix[0] = 0;
-  for (int base = 0; base < G; base += T) {
-    const int p = base + tid;
-    int cnt = 0;
-    if (p < G) {
-      const int rows = rows_of[expert_at[p]];
-      cnt = rows > 0 ? (rows + BM - 1) / BM : 0;
+  // Prefix over tile-order positions of the number of BM-row tiles, by one
+  // wave: lane l covers positions 16l .. 16l+15 (a lane sum, a shuffle scan
+  // over the lanes, then the lane's 16 prefix values).
+  if (tid < 64) {
+    constexpr int PL = kMaxExpertsLds / 64;
+    const int p0 = lane * PL;
+    int sum = 0;
+    for (int i = 0; i < PL; ++i)
+      if (p0 + i < G) sum += mtiles(rows_of[expert_at[p0 + i]]);
+    int inc = sum;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(inc, d);
+      if (lane >= d) inc += v;
     }
-    scan[tid] = cnt;
-    __syncthreads();
-    for (int d = 1; d < T; d <<= 1) {
-      const int add = tid >= d ? scan[tid - d] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
+    int run = inc - sum;
+    if (lane == 0) mt_prefix[0] = 0;
+    for (int i = 0; i < PL; ++i)
+      if (p0 + i < G) {
+        run += mtiles(rows_of[expert_at[p0 + i]]);
+        mt_prefix[p0 + i + 1] = run;
+      }
+  }
+  __syncthreads();
+  // Lane r of every wave maps this workgroup's round-r tile to (expert,
+  // m-tile, n-tile): tile-order position p with prefix[p] <= m-tile index <
+  // prefix[p+1].  Real tiles are numbered in tile order, m-tile, then n-tile
+  // fastest.
+  int my_e = 0, my_mt = 0, my_tn = 0;
+  const int j = lane * K8 + ((lane & 1) ? K8 - 1 - k : k);
+  const bool has = j < len;
+  if (has) {
+    const int id = run0 + j;
+    const int mt_global = id / tiles_n;
+    my_tn = id % tiles_n;
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (mt_prefix[mid] <= mt_global) lo = mid; else hi = mid;
     }
-    if (p < G) mt_prefix[p + 1] = running + scan[tid];
-    running += scan[T - 1];
-    __syncthreads();
+    my_e = expert_at[lo];
+    my_mt = mt_global - mt_prefix[lo];
   }
-  const int total = running * tiles_n;  // real tiles
-  const int bid = blockIdx.x;
-  if (bid >= total) return;
-  // XCD-contiguous numbering of the real tiles: bid -> id is a bijection on
-  // [0, total); XCD x (= bid mod 8) receives ids [x*q + min(x, r), ...).
-  const int q8 = total / kXcds, r8 = total % kXcds;
-  const int x = bid % kXcds;
-  const int id = x * q8 + (x < r8 ? x : r8) + bid / kXcds;
-  const int mt_global = id / tiles_n;
-  const int tn = id % tiles_n;
-  // position p with prefix[p] <= mt_global < prefix[p+1]
-  int lo = 0, hi = G;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (mt_prefix[mid] <= mt_global) lo = mid; else hi = mid;
-  }
-  const int e = expert_at[lo];
-  const int mt = mt_global - mt_prefix[lo];
-  const int64_t r0 = off[e];
-  const int64_t r1 = off[e + 1];
-  __syncthreads();  // mt_prefix is overwritten by the mainloop
+  // Rounds with a tile are a prefix of the lanes (j grows with the lane).
+  const int n_mine = __builtin_popcountll(__ballot(has));
+  __syncthreads();  // the prefix scratch is overwritten by the tiles' rings
 
-  TileArgs t;
-  t.A = A;
-  t.SA = SA;
-  t.W = W + (int64_t)e * N * K;
-  t.SW = SW + (int64_t)e * (N / 128) * (K / 128);
-  t.a_row0 = r0 + (int64_t)mt * BM;
-  t.a_rows = r1;
-  t.w_row0 = (int64_t)tn * kGroupedBN;
-  t.w_rows = N;
-  t.K = K;
-  t.sa_ld = M_total;
-  t.C = C;
-  t.ldc = N;
-  t.out_bf16 = out_bf16;
-  const int64_t live = r1 - t.a_row0;  // 1 .. (>= 256 when more m-tiles follow)
-  if (live <= 64)
-    gemm_tile<GroupedCfg<64, kS64>>(t, smem);
-  else if (live <= 128)
-    gemm_tile<GroupedCfg<128, kS128>>(t, smem);
-  else if (live <= 160)
-    gemm_tile<GroupedCfg<160, kS160>>(t, smem);
-  else if (live <= 192)
-    gemm_tile<GroupedCfg<192, kS192>>(t, smem);
-  else
-    gemm_tile<GroupedCfg<256, kS256>>(t, smem);
+  for (int r = 0; r < n_mine; ++r) {
+    const int e = __builtin_amdgcn_readlane(my_e, r);
+    const int mt = __builtin_amdgcn_readlane(my_mt, r);
+    const int tn = __builtin_amdgcn_readlane(my_tn, r);
+    const int64_t r0 = off[e];
+    const int64_t r1 = off[e + 1];
+    TileArgs t;
+    t.A = A;
+    t.SA = SA;
+    t.W = W + (int64_t)e * N * K;
+    t.SW = SW + (int64_t)e * (N / 128) * (K / 128);
+    t.a_row0 = r0 + (int64_t)mt * BM;
+    t.a_rows = r1;
+    t.w_row0 = (int64_t)tn * kGroupedBN;
+    t.w_rows = N;
+    t.K = K;
+    t.sa_ld = M_total;
+    t.C = C;
+    t.ldc = N;
+    t.out_bf16 = out_bf16;
+    const int64_t live = r1 - t.a_row0;  // 1 .. (>= 256 when more m-tiles follow)
+    if (live <= 64)
+      gemm_tile<GroupedCfg<64, kS64>>(t, smem);
+    else if (live <= 128)
+      gemm_tile<GroupedCfg<128, kS128>>(t, smem);
+    else if (live <= 160)
+      gemm_tile<GroupedCfg<160, kS160>>(t, smem);
+    else if (live <= 192)
+      gemm_tile<GroupedCfg<192, kS192>>(t, smem);
+    else
+      gemm_tile<GroupedCfg<256, kS256>>(t, smem);
+    __syncthreads();  // the next tile's loads reuse the ring
+  }
 }
 
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
@@ -647,12 +675,19 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
   const int64_t max_mtiles = M_total / 256 + G;
   const int64_t tiles = max_mtiles * tiles_n;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  // The largest-first order applies up to 4 tiles per CU of the device.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipGetLastError();
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)tiles), dim3(kGroupedThreads), 0,
+  // Persistent grid: one workgroup per CU (LDS allows one), 8 per XCD
+  // round, and enough of them that no workgroup walks more than 64 rounds of
+  // its XCD's run (at most ceil(tiles / 8) tiles).
+  const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+  int64_t k8 = (cus + kXcds - 1) / kXcds;
+  if (k8 < (per_xcd + 63) / 64) k8 = (per_xcd + 63) / 64;
+  const int64_t grid = k8 * kXcds;
+  // The largest-first order applies up to 4 tiles per CU of the device.
+  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)grid), dim3(kGroupedThreads), 0,
                      stream, a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16,
                      (int)tiles_n, 4 * cus);
   return hipGetLastError();
