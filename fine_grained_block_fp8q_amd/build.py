@@ -1,7 +1,9 @@
 """Build libfp8q.so (gfx950) in-tree with hipcc.
 
-Usage: python -m fine_grained_block_fp8q_amd.build   (or call build()).
-The library lands next to this file; the Python binding loads it from there.
+Usage: python fine_grained_block_fp8q_amd/build.py   (or load this file and
+call build(); importing it through the package would first load the library
+it builds).  The library lands next to this file; the Python binding loads it
+from there.
 """
 
 import os

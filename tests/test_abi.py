@@ -24,7 +24,7 @@ def _declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libfp8q.so is not built (python -m fine_grained_block_fp8q_amd.build)")
+        pytest.fail("libfp8q.so is not built (python fine_grained_block_fp8q_amd/build.py)")
     L = ctypes.CDLL(LIB)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.fp8q_quantize_act.argtypes = [p, i64, i64, p, p, i32, p]
