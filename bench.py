@@ -10,6 +10,10 @@ One step = one pass of the whole path over one batch of synthetic input:
   decode:          activation quantization of ~4352 rows + grouped GEMM over 32
                    experts (M_e uniform in [16, 256]), BF16 output.
   largek:          activation + weight quantization of 8192 x 65536 each + GEMM.
+  bf16:            the comparison the pages' speed claim calls for: the BF16 GEMM
+                   of the same kernel family on the dense shape (BF16 A and W,
+                   FP32 out); the FP8 GEMM on the same inputs, quantized once,
+                   and hipBLASLt's BF16 matmul (torch.matmul) are timed beside it.
 
 Inputs are resident in HBM before the timed region; several input sets are
 rotated so that every step streams its inputs from HBM rather than from the
@@ -33,6 +37,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+METRIC_BF16 = "BF16 GEMM TFLOP/s (% BF16 MFMA peak), the reference of the FP8 path"
+
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 ACT_BYTES_PER_ELEM = 2 + 1 + 4 / 128          # BF16 in, E4M3 out, one FP32 scale per 128
 WEIGHT_BYTES_PER_ELEM = 2 + 1 + 4 / 16384     # one FP32 scale per 128x128 block
@@ -43,7 +50,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "moe", "decode", "largek"])
+    p.add_argument("--workload", default="dense", choices=["dense", "moe", "decode", "largek", "bf16"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -112,6 +119,53 @@ def setup_dense(fq, torch, name, sets):
     flops = 2.0 * M * N * K
     cfg = {"workload": f"{name}: A {M}x{K} bf16 (1x128 act quant), W {N}x{K} bf16 "
                        f"(128x128 block quant), C = A W^T fp32",
+           "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
+    return step, launch, kernels, flops, cfg
+
+
+def setup_bf16(fq, torch, sets):
+    import workloads
+    c = workloads.WORKLOADS["dense"]
+    M, N, K = c["M"], c["N"], c["K"]
+    dev = "cuda:0"
+    A_bits, W_bits = workloads.dense_inputs("dense")
+    A0 = torch.from_numpy(A_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    W0 = torch.from_numpy(W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    del A_bits, W_bits
+    bufs = []
+    for i in range(sets):
+        A = A0 if i == 0 else A0.clone()
+        W = W0 if i == 0 else W0.clone()
+        Wt = W.t().contiguous()  # [K][N] for torch.matmul (no transposed views)
+        aq, as_ = fq.quantize_act(A)
+        wq, ws = fq.quantize_weight(W)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        Cb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        bufs.append((A, W, Wt, aq, as_, wq, ws, C, Cb))
+
+    def launch(name, i):
+        A, W, Wt, aq, as_, wq, ws, C, Cb = bufs[i % sets]
+        if name == "fp8q_gemm_bf16":
+            fq.fp8q_gemm_bf16(A, W, C)
+        elif name == "fp8q_gemm_bf16_bf16out":
+            fq.fp8q_gemm_bf16(A, W, Cb)
+        elif name == "fp8q_gemm":
+            fq.fp8q_gemm(aq, as_, wq, ws, C)
+        else:  # hipBLASLt through torch, BF16 out
+            torch.matmul(A, Wt, out=Cb)
+
+    def step(i):
+        launch("fp8q_gemm_bf16", i)
+
+    flops = 2.0 * M * N * K
+    kernels = [
+        ("fp8q_gemm_bf16", "mfma_bf16", flops, "flop"),
+        ("fp8q_gemm_bf16_bf16out", "mfma_bf16", flops, "flop"),
+        ("torch_matmul_bf16_hipblaslt", "mfma_bf16", flops, "flop"),
+        ("fp8q_gemm", "mfma", flops, "flop"),
+    ]
+    cfg = {"workload": f"bf16: A {M}x{K} bf16, W {N}x{K} bf16, C = A W^T fp32 (BF16 GEMM of "
+                       f"the FP8 kernel family; the dense workload's inputs)",
            "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
     return step, launch, kernels, flops, cfg
 
@@ -226,6 +280,18 @@ def cpu_baseline(name):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    if name == "bf16":
+        c = workloads.WORKLOADS["dense"]
+        M, N, K = c["M"], c["N"], c["K"]
+        A, W = workloads.dense_inputs("dense")
+        t0 = time.perf_counter()
+        ogemm.gemm_bf16(A, W)
+        dt = time.perf_counter() - t0
+        return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+                "kind": "oracle",
+                "sample": f"the whole bf16 workload: oracle gemm_bf16 (float64 matmul of "
+                          f"the BF16 values) {M}x{N}x{K}; {dt:.1f} s wall; "
+                          f"value = 2*M*N*K / wall"}
     c = workloads.WORKLOADS[name]
     if name == "dense":
         M, N, K = c["M"], c["N"], c["K"]
@@ -265,9 +331,12 @@ def main():
     import torch
     import fine_grained_block_fp8q_amd as fq
 
-    sets = args.sets or (4 if args.workload in ("dense",) else 2 if args.workload == "decode" else 1)
+    sets = args.sets or (4 if args.workload in ("dense", "bf16") else
+                         2 if args.workload == "decode" else 1)
     if args.workload in ("dense", "largek"):
         step, launch, kernels, flops, cfg = setup_dense(fq, torch, args.workload, sets)
+    elif args.workload == "bf16":
+        step, launch, kernels, flops, cfg = setup_bf16(fq, torch, sets)
     else:
         step, launch, kernels, flops, cfg = setup_grouped(fq, torch, args.workload, sets)
     torch.cuda.synchronize()
@@ -289,6 +358,8 @@ def main():
     # median and the 10th / 90th percentiles.
     kout = {}
     for kname, bound, work, unit in kernels:
+        launch(kname, 0)  # first call of a library kernel includes its set-up
+        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -314,10 +385,23 @@ def main():
                            "bytes": work, **spread}
         else:
             ach = work / (avg_ms * 1e-3) / 1e12
-            kout[kname] = {"avg_us": avg_ms * 1e3, "TFLOP_s": ach,
-                           "frac_fp8_peak": ach / PEAK_FP8_TFLOPS, "flops": work, **spread}
+            peak_key, peak = (("frac_bf16_peak", PEAK_BF16_TFLOPS) if bound == "mfma_bf16"
+                              else ("frac_fp8_peak", PEAK_FP8_TFLOPS))
+            kout[kname] = {"avg_us": avg_ms * 1e3, "TFLOP_s": ach, peak_key: ach / peak,
+                           "flops": work, **spread}
 
-    if args.workload in ("dense", "largek"):
+    if args.workload == "bf16":
+        dom = kout["fp8q_gemm_bf16"]
+        roof = {"kernel": "fp8q_gemm_bf16", "bound": "mfma", "achieved": dom["TFLOP_s"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom["TFLOP_s"] / PEAK_BF16_TFLOPS,
+                "traffic": recorded_traffic("fp8q_gemm_bf16", cfg)}
+        # The pages' claim, measured: FP8 GEMM speed over BF16 GEMM speed.
+        roof["fp8_speedup_over_bf16"] = {
+            "same_kernel_family": dom["avg_us"] / kout["fp8q_gemm"]["avg_us"],
+            "hipblaslt_bf16_out": (kout["torch_matmul_bf16_hipblaslt"]["avg_us"]
+                                   / kout["fp8q_gemm"]["avg_us"])}
+    elif args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm"]
         traffic = recorded_traffic("fp8q_gemm", cfg)
         roof = {"kernel": "fp8q_gemm", "bound": "mfma", "achieved": dom["TFLOP_s"],
@@ -332,9 +416,11 @@ def main():
                 "traffic": recorded_traffic("fp8q_grouped_gemm", cfg)}
 
     value = flops / (ms_per_step * 1e-3) / 1e12
-    rec = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+    bf16 = args.workload == "bf16"
+    rec = {"metric": METRIC_BF16 if bf16 else METRIC, "value": value, "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if bf16 else "fp8e4m3",
            "data": "synthetic (seeded; shapes and distributions of the workload table)",
            "config": cfg, "roofline": roof, "kernels": kout}
     if not args.no_cpu_baseline:

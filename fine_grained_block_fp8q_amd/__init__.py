@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libfp8q.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libfp8q.so not found at {LIB_PATH}; build it with "
-        "`python -m fine_grained_block_fp8q_amd.build` (hipcc, gfx950)")
+        "`python fine_grained_block_fp8q_amd/build.py` (hipcc, gfx950)")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -38,6 +38,8 @@ lib.fp8q_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_gemm.restype = _st
 lib.fp8q_grouped_gemm.argtypes = [_p, _p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32, _p]
 lib.fp8q_grouped_gemm.restype = _st
+lib.fp8q_gemm_bf16.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i32, _p]
+lib.fp8q_gemm_bf16.restype = _st
 lib.fp8q_status_string.argtypes = [_st]
 lib.fp8q_status_string.restype = ctypes.c_char_p
 lib.fp8q_abi_version.argtypes = []
@@ -113,6 +115,16 @@ def fp8q_grouped_gemm(a_q, a_s, off, w_q, w_s, c, stream=None):
     _check(lib.fp8q_grouped_gemm(_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
                                  _ptr(w_s), N, K, _ptr(c), out, _stream(stream, a_q.device)),
            "fp8q_grouped_gemm")
+
+
+def fp8q_gemm_bf16(a, w, c, stream=None):
+    """c[M][N] (float32 or bfloat16) = a[M][K] x w[N][K]^T, BF16 operands."""
+    import torch
+    M, K = a.shape
+    N = w.shape[0]
+    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    _check(lib.fp8q_gemm_bf16(_ptr(a), _ptr(w), M, N, K, _ptr(c), out, _stream(stream, a.device)),
+           "fp8q_gemm_bf16")
 
 
 # ---------------------------------------------------------- allocation helpers

@@ -22,6 +22,8 @@ hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
                                const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
                                int64_t N, int64_t K, void* c, int out_bf16, hipStream_t stream);
+hipError_t launch_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
+                            void* c, int out_bf16, hipStream_t stream);
 }  // namespace fp8q
 
 namespace {
@@ -164,6 +166,22 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c,
                                             out == FP8Q_OUT_BF16, stream));
+}
+
+fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
+                           void* c, fp8q_out_dtype out, hipStream_t stream) {
+  const bool empty_out = (M == 0 || N == 0);
+  if (!empty_out && !c) return FP8Q_ERR_NULL;
+  if (!empty_out && K != 0 && (!a || !w)) return FP8Q_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(a, 16) || !aligned(w, 16) || !aligned(c, 16)) return FP8Q_ERR_ALIGN;
+  if (!valid_out(out)) return FP8Q_ERR_ENUM;
+  if (empty_out) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_UNSUPPORTED;
+  if (K > (int64_t(1) << 21)) return FP8Q_ERR_UNSUPPORTED;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_gemm_bf16(a, w, M, N, K, c, out == FP8Q_OUT_BF16, stream));
 }
 
 }  // extern "C"

@@ -36,12 +36,18 @@
 
 namespace fp8q {
 
+// OP_BF16_: BF16 operands (the reference GEMM of the same kernel family):
+// a 128-byte stage row then holds 64 K values, each 16x16 block takes two
+// chained 16x16x32 BF16 MFMAs per chunk, accumulating in the matrix core (its
+// BF16 path accumulates to FP32 accuracy), and there are no scales.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int ROWS_ = BM_,
-          int PF_ = 0>
+          int PF_ = 0, int OP_BF16_ = 0>
 struct GemmCfg {
+  static constexpr bool OP_BF16 = OP_BF16_ != 0;
+  static constexpr int SUB = OP_BF16 ? 2 : 1;       // MFMAs per 16x16 block per chunk
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
-  static constexpr int BK = 128;                    // one promotion interval
+  static constexpr int BK = 128;                    // bytes of K per stage row and chunk
   static constexpr int WAVES_M = WAVES_M_;
   static constexpr int WAVES_N = WAVES_N_;
   static constexpr int NWAVES = WAVES_M * WAVES_N;
@@ -53,7 +59,7 @@ struct GemmCfg {
   static constexpr int ROWS = ROWS_;                // A rows staged per chunk (<= BM)
   static constexpr int A_BYTES = ROWS * BK;
   static constexpr int B_BYTES = BN * BK;
-  static constexpr int SA_BYTES = WAVES_M * 256;    // up to 64 row scales per row of waves
+  static constexpr int SA_BYTES = OP_BF16 ? 0 : WAVES_M * 256;  // 64 row scales per row of waves
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
@@ -63,7 +69,7 @@ struct GemmCfg {
   static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
   static constexpr int PER_WAVE = (OP_BLK + NWAVES - 1) / NWAVES;  // operand loads per wave
   static constexpr int PAD = PER_WAVE * NWAVES - OP_BLK;  // repeated A loads that even them out
-  static constexpr int LOADS = PER_WAVE + 1;        // + the scale slot
+  static constexpr int LOADS = PER_WAVE + (OP_BF16 ? 0 : 1);  // + the scale slot
   static_assert(WM % 16 == 0 && WM <= 64, "a wave's rows fit one 256-byte scale slot");
   static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
   // Staged rows: whole 1 KiB loads.  When they stop inside a wave (160 rows
@@ -83,6 +89,8 @@ struct GemmCfg {
 // L2 prefetch kPfDist chunks ahead (a ring of 2 stages leaves the loads of a
 // chunk less than one chunk's compute time to arrive from HBM).
 using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
+// The BF16 GEMM: the same tile, waves, ring and prefetch.
+using DenseBf16Cfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 1>;
 // Grouped configurations: 256-row tiles cover an expert's tokens (decode
 // batches hold at most 256) so each expert's weights stream once, and 256
 // weight rows per tile (8 waves of 64 x 128, as in the dense tile) so each
@@ -159,9 +167,11 @@ struct ChunkLoader {
     const int64_t w_live = t.w_rows - t.w_row0;  // >= 1
     ra = make_rsrc(t.A + t.a_row0 * t.K, a_live * t.K);
     rw = make_rsrc(t.W + t.w_row0 * t.K, w_live * t.K);
-    const int64_t G = t.K / Cfg::BK;
-    rs = make_rsrc(t.SA + t.a_row0, (G * t.sa_ld - t.a_row0) * 4);
-    s_stride = t.sa_ld * 4;
+    if constexpr (!Cfg::OP_BF16) {
+      const int64_t G = t.K / Cfg::BK;
+      rs = make_rsrc(t.SA + t.a_row0, (G * t.sa_ld - t.a_row0) * 4);
+      s_stride = t.sa_ld * 4;
+    }
     const int sub_r = lane >> 3;
     const int pc = lane & 7;
 #pragma unroll
@@ -177,8 +187,10 @@ struct ChunkLoader {
     // rows (up to 64; rows past them are loaded and not used), so the scales
     // an MFMA column lane needs (rows c, 16 + c, 32 + c, 48 + c) sit side by
     // side in LDS.
-    const int64_t rs_row = wave_m_ * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
-    voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
+    if constexpr (!Cfg::OP_BF16) {
+      const int64_t rs_row = wave_m_ * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
+      voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
+    }
     // L2 prefetch lines.  The XCD-aware tile order gives one XCD a block of
     // 4 tile rows x 8 tile columns, so 8 tiles share each 256-row A band and
     // 4 share each W band in that XCD's L2.  A tile therefore prefetches
@@ -210,13 +222,25 @@ struct ChunkLoader {
       const int dst = is_a ? m * 1024 : Cfg::A_BYTES + (m - Cfg::A_BLK) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rw, to_lds(stage + dst), 16, voff[d],
                                                (int)(g * Cfg::BK), 0, 0);
-    } else {
+    } else if constexpr (!Cfg::OP_BF16) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256), 4, voff_s,
           (int)(g * s_stride), 0, 0);
     }
   }
 };
+
+// One 32-K half of a chunk for BF16 operands: fragment half h (the 16-byte
+// piece q, or q + 4, of the 128-byte row, i.e. 8 BF16 values per lane) of the
+// weight and activation fragments, accumulated into acc by the matrix core.
+__device__ __forceinline__ v4f mfma_bf16_half(const v8i& w, const v8i& a, const v4f& acc,
+                                              int h) {
+  typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+  const v4i wh = h ? v4i{w[4], w[5], w[6], w[7]} : v4i{w[0], w[1], w[2], w[3]};
+  const v4i ah = h ? v4i{a[4], a[5], a[6], a[7]} : v4i{a[0], a[1], a[2], a[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wh),
+                                                 __builtin_bit_cast(v8bf, ah), acc, 0, 0, 0);
+}
 
 // Promotion of one 16x16 chunk partial: acc += P * (s_a[row] * s_w).
 __device__ __forceinline__ void promote(v4f& acc, const v4f& p, float mult) {
@@ -231,6 +255,7 @@ __device__ __forceinline__ void promote(v4f& acc, const v4f& p, float mult) {
 template <class Cfg>
 __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   constexpr int MB = Cfg::MB, NB = Cfg::NB, S = Cfg::STAGES;
+  constexpr int RB = MB * Cfg::SUB;  // MFMA steps per weight row block
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_m = wave / Cfg::WAVES_N;
@@ -240,10 +265,13 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   const int64_t G = t.K / Cfg::BK;
 
   // Weight-scale row of this wave's weight rows (one 128-row block).
-  int64_t wblk = (t.w_row0 + wave_n * Cfg::WN) / 128;
-  const int64_t last_wblk = t.w_rows / 128 - 1;
-  wblk = wblk < last_wblk ? wblk : last_wblk;
-  const float* sw_row = t.SW + wblk * G;
+  const float* sw_row = nullptr;
+  if constexpr (!Cfg::OP_BF16) {
+    int64_t wblk = (t.w_row0 + wave_n * Cfg::WN) / 128;
+    const int64_t last_wblk = t.w_rows / 128 - 1;
+    wblk = wblk < last_wblk ? wblk : last_wblk;
+    sw_row = t.SW + wblk * G;
+  }
 
   // Waves whose rows are all past the valid range skip the MFMA work.
   const bool wave_live =
@@ -267,26 +295,29 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   //                    MFMA of chunk g it is refilled with chunk g+1's data,
   //                    so chunk g+1 starts with its operands in registers.
   // Step k is MFMA (weight row block j = k / MB, activation block i = k % MB):
-  // one weight fragment serves MB consecutive MFMAs.
+  // one weight fragment serves MB consecutive MFMAs.  With BF16 operands a
+  // block takes SUB = 2 MFMAs per chunk (the chunk's two 32-K halves): row
+  // block j runs steps RB*j .. RB*j + RB - 1, first half h = 0 for the MB
+  // activation blocks, then h = 1, so chained MFMAs are MB steps apart.
   // The matrix core therefore never waits for a chunk boundary: a wave that
   // arrives early at the barrier leaves the matrix core to its SIMD partner.
-  constexpr int LAG = kPromoteLag;
-  constexpr int KSTEPS = MB * NB + LAG;
-  constexpr int kBar = MB * (NB - 1) - kBarLead;   // before the last row block
+  constexpr int LAG = Cfg::OP_BF16 ? 0 : kPromoteLag;
+  constexpr int KSTEPS = RB * NB + LAG;
+  constexpr int kBar = RB * (NB - 1) - kBarLead;   // before the last row block
   constexpr int TAIL = KSTEPS - 1 - kBar;          // loads issued after the barrier
   constexpr int D1 = TAIL < Cfg::LOADS ? TAIL : Cfg::LOADS;
   // Weight fragments are read BPF row blocks ahead into a ring of BPF+1 slots.
   constexpr int BPF = kBPrefetch;
   constexpr int NBUF = BPF + 1;
-  static_assert(kBar > MB * (NB - 1 - BPF), "the barrier follows the last weight read");
-  static_assert(kBar < MB * (NB - 1), "the barrier precedes the last row block");
+  static_assert(kBar > RB * (NB - 1 - BPF), "the barrier follows the last weight read");
+  static_assert(kBar < RB * (NB - 1), "the barrier precedes the last row block");
   // Step after which weight slot t (t < BPF) is free for chunk g+1's block t: the
   // last MFMA of the last block j < NB with j % NBUF == t, but not before the
   // barrier.
   auto next_b_step = [](int t) constexpr {
     int jt = t;
     while (jt + NBUF < NB) jt += NBUF;
-    const int kt = MB * jt + MB - 1;
+    const int kt = RB * jt + RB - 1;
     return kt > kBar ? kt : kBar;
   };
   static_assert(kDma0 + (Cfg::LOADS - D1 - 1) * kDmaStep < kBar,
@@ -361,22 +392,28 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
     }
 
     const uint8_t* Bs = st_cur + Cfg::A_BYTES;
-    const float* SAs =
-        reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256);
-    const float sw = sw_row[g];
-    const v4f sa = *reinterpret_cast<const v4f*>(SAs + 4 * r16);
     float mult[MB];
+    if constexpr (!Cfg::OP_BF16) {
+      const float* SAs =
+          reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256);
+      const float sw = sw_row[g];
+      const v4f sa = *reinterpret_cast<const v4f*>(SAs + 4 * r16);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) mult[i] = sa[i] * sw;
+      for (int i = 0; i < MB; ++i) mult[i] = sa[i] * sw;
+    }
     v4f p[LAG + 1];
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k) {
-      if (k < MB * NB) {
-        const int i = k % MB, j = k / MB;
-        if (i == 0 && j + BPF < NB)
+      if (k < RB * NB) {
+        const int i = k % MB, h = (k / MB) % Cfg::SUB, j = k / RB;
+        if (k % RB == 0 && j + BPF < NB)
           b[(j + BPF) % NBUF] = load_frag(Bs, wave_n * Cfg::WN + (j + BPF) * 16 + r16, q);
-        p[k % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            b[j % NBUF], a[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if constexpr (Cfg::OP_BF16) {
+          acc[i][j] = mfma_bf16_half(b[j % NBUF], a[i], acc[i][j], h);
+        } else {
+          p[k % (LAG + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              b[j % NBUF], a[i], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int d = D1; d < Cfg::LOADS; ++d)
@@ -388,13 +425,14 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
         wait_vmcnt<kAfter>();  // chunk g+1 landed
         lds_barrier();
       }
-      if (k < MB * NB) {
+      if (k < RB * NB) {
         // Chunk g+1's fragments go into registers as soon as their chunk-g
         // contents have served their last MFMA (and the barrier at kBar has
-        // made chunk g+1 visible): a[i] after row block NB-1's MFMA i, weight slot t
-        // after the last block of chunk g that uses it.
-        const int i = k % MB, j = k / MB;
-        if (j == NB - 1) a[i] = load_frag(st_nxt, wave_m * Cfg::WM + i * 16 + r16, q);
+        // made chunk g+1 visible): a[i] after row block NB-1's last MFMA with
+        // it, weight slot t after the last block of chunk g that uses it.
+        const int i = k % MB, h = (k / MB) % Cfg::SUB, j = k / RB;
+        if (j == NB - 1 && h == Cfg::SUB - 1)
+          a[i] = load_frag(st_nxt, wave_m * Cfg::WM + i * 16 + r16, q);
 #pragma unroll
         for (int t = 0; t < BPF; ++t)
           if (k == next_b_step(t))
@@ -408,8 +446,10 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
       // MFMA (to hand its result registers to MFMA k), which leaves it right
       // behind MFMA k-LAG+1 and stalls the wave on the matrix core's result.
       __builtin_amdgcn_sched_barrier(0);
-      const int kp = k - LAG;
-      if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
+      if constexpr (!Cfg::OP_BF16) {
+        const int kp = k - LAG;
+        if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     cur = nxt;
@@ -648,6 +688,21 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
       gemm_tile<GroupedCfg<256, kS256>>(t, smem);
     __syncthreads();  // the next tile's loads reuse the ring
   }
+}
+
+hipError_t launch_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
+                            void* c, int out_bf16, hipStream_t stream) {
+  using Cfg = DenseBf16Cfg;
+  if (M == 0 || N == 0) return hipSuccess;
+  const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+  const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // Operand rows are 2K bytes: the kernel's K is the row length in bytes.
+  hipLaunchKernelGGL(gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(a), nullptr, static_cast<const uint8_t*>(w),
+                     nullptr, M, N, 2 * K, c, out_bf16, (int)tiles_n);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,

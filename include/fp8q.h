@@ -149,6 +149,25 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
                               int64_t N, int64_t K,
                               void* c, fp8q_out_dtype out, hipStream_t stream);
 
+/*
+ * BF16 GEMM of the same kernel family, without quantization: the reference
+ * point for the FP8 path's speed (the-good.kr post 2169793, mixed-precision
+ * framework passage: running the GEMMs in FP8 is said to double their speed
+ * in theory over BF16) and accuracy.
+ *   C[m][n] = sum_k a[m][k] * w[n][k]
+ *   a : [M][K] bfloat16, w : [N][K] bfloat16, row-major; 16-byte aligned.
+ *   c : [M][N] float32 or bfloat16 (per `out`), row-major (output).
+ *   M >= 0, N % 128 == 0, K % 128 == 0 (the shape rules of fp8q_gemm).
+ * FP8Q_ERR_UNSUPPORTED: K == 0 with M*N > 0, or K > 2^21 (32-bit load
+ *   offsets over rows of 2K bytes).
+ * Accuracy: the products of BF16 values are exact in FP32; the matrix core
+ * accumulates them (32 per instruction, with the running sum as its C input)
+ * to FP32 accuracy, so |C - C_exact| <= 1e-5 * sum_k |a[m][k]| * |w[n][k]|
+ * (plus half a BF16 ulp for BF16 output).
+ */
+fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
+                           void* c, fp8q_out_dtype out, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fp8q_status_string(fp8q_status status);
 

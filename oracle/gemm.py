@@ -79,6 +79,27 @@ def grouped_gemm(qa, sa, offsets, qw, sw):
     return C
 
 
+def gemm_bf16(a_bits, w_bits):
+    """BF16 reference GEMM: C (float64[M][N]) = sum_k a[m][k] * w[n][k].
+
+    a_bits: uint16[M][K], w_bits: uint16[N][K] BF16 bit patterns.  This is the
+    unquantized product the FP8 path is measured against ([goodkr-2169793],
+    mixed-precision framework passage: FP8 GEMMs in place of BF16 ones).  A
+    BF16 value has 8 significant bits, so every product is exact in float64;
+    the sum over K rounds at 2^-53 relative to the running sum.
+    """
+    from .quant import bf16_bits_to_f32
+    a = bf16_bits_to_f32(a_bits).astype(np.float64)
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    return a @ w.T
+
+
+def abs_bound_bf16(a_bits, w_bits):
+    """sum_k |a[m][k]| * |w[n][k]| (float64[M][N]), for the 1e-5 tolerance."""
+    return gemm_bf16(np.asarray(a_bits, np.uint16) & np.uint16(0x7FFF),
+                     np.asarray(w_bits, np.uint16) & np.uint16(0x7FFF))
+
+
 def round_to_f32(c):
     """RNE of float64 values to float32 (numpy's cast is RNE)."""
     return np.asarray(c, dtype=np.float64).astype(np.float32)

@@ -18,7 +18,7 @@ OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_DEVICE, E_LAUNCH, E_UNSUP = range(8)
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fp8q_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -31,6 +31,7 @@ def lib():
     L.fp8q_quantize_weight.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_grouped_gemm.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
+    L.fp8q_gemm_bf16.argtypes = [p, p, i64, i64, i64, p, i32, p]
     L.fp8q_status_string.restype = ctypes.c_char_p
     L.fp8q_status_string.argtypes = [ctypes.c_int]
     return L
@@ -46,7 +47,8 @@ def _no_device():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm",
-                          "fp8q_grouped_gemm", "fp8q_status_string", "fp8q_abi_version"}
+                          "fp8q_grouped_gemm", "fp8q_gemm_bf16", "fp8q_status_string",
+                          "fp8q_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -122,6 +124,23 @@ def test_grouped_gemm_validation(lib):
     assert f(None, None, 0, A, 2, None, None, 128, 128, None, 0, None) == OK
 
 
+def test_gemm_bf16_validation(lib):
+    f = lib.fp8q_gemm_bf16
+    assert f(A, A, 4, 128, 128, None, 0, None) == E_NULL
+    assert f(None, A, 4, 128, 128, A, 0, None) == E_NULL
+    assert f(A, None, 4, 128, 128, A, 0, None) == E_NULL
+    assert f(A, A, 4, 100, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, 4, 128, 64, A, 0, None) == E_SHAPE
+    assert f(A, A, -4, 128, 128, A, 0, None) == E_SHAPE
+    assert f(A + 2, A, 4, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A + 8, 4, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A, 4, 128, 128, A + 4, 0, None) == E_ALIGN
+    assert f(A, A, 4, 128, 128, A, 2, None) == E_ENUM
+    assert f(None, None, 0, 128, 128, None, 0, None) == OK
+    assert f(A, A, 4, 128, 0, A, 0, None) == E_UNSUP                  # K == 0: C = 0
+    assert f(A, A, 4, 128, (1 << 21) + 128, A, 0, None) == E_UNSUP    # 2K-byte rows
+
+
 def test_valid_arguments_without_gpu_report_device_error(lib):
     if not _no_device():
         pytest.skip("a GPU is visible: fake pointers must not be launched")
@@ -129,3 +148,4 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert lib.fp8q_quantize_weight(A, 128, 128, A, A, 1, None) == E_DEVICE
     assert lib.fp8q_gemm(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
     assert lib.fp8q_grouped_gemm(A, A, 8, A, 2, A, A, 128, 128, A, 0, None) == E_DEVICE
+    assert lib.fp8q_gemm_bf16(A, A, 4, 128, 128, A, 0, None) == E_DEVICE

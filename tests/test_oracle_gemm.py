@@ -138,3 +138,40 @@ def test_bf16_rounding_helpers():
     ref = torch.tensor(v, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(r, ref)
     assert gemm.bf16_half_ulp(np.array([1.0]))[0] == 2.0 ** -8
+
+
+def test_bf16_reference_exact_rational_bruteforce():
+    """gemm_bf16 against exact rational sums of the BF16 values (tiny shape,
+    signed values, an x50 outlier column)."""
+    rng = np.random.default_rng(41)
+    M, N, K = 5, 7, 256
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[:, 3] *= 50
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A = workloads.bf16_bits(a)
+    W = workloads.bf16_bits(w)
+    C = gemm.gemm_bf16(A, W)
+    bound = gemm.abs_bound_bf16(A, W)
+    av = quant.bf16_bits_to_f32(A)
+    wv = quant.bf16_bits_to_f32(W)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(av[m, k])) * Fraction(float(wv[n, k])) for k in range(K))
+            assert abs(Fraction(float(C[m, n])) - exact) <= Fraction(float(bound[m, n])) * Fraction(K, 2**53)
+            # the bound itself is the sum of magnitudes
+            mag = sum(abs(Fraction(float(av[m, k])) * Fraction(float(wv[n, k]))) for k in range(K))
+            assert abs(Fraction(float(bound[m, n])) - mag) <= mag * Fraction(K, 2**53)
+
+
+def test_bf16_reference_permutation_picks_columns():
+    """W = a permutation matrix P (w[n][k] = 1 iff k = p[n]): C[m][n] = a[m][p[n]].
+    A transposed operand or a swapped index would pick the wrong entries."""
+    rng = np.random.default_rng(42)
+    M, K = 9, 384
+    N = 128
+    a = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    p = rng.permutation(K)[:N]
+    w = np.zeros((N, K), dtype=np.float32)
+    w[np.arange(N), p] = 1.0
+    C = gemm.gemm_bf16(a, workloads.bf16_bits(w))
+    assert np.array_equal(C, quant.bf16_bits_to_f32(a)[:, p].astype(np.float64))
