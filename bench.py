@@ -147,8 +147,6 @@ def setup_bf16(fq, torch, sets):
         A, W, Wt, aq, as_, wq, ws, C, Cb = bufs[i % sets]
         if name == "fp8q_gemm_bf16":
             fq.fp8q_gemm_bf16(A, W, C)
-        elif name == "fp8q_gemm_bf16_bf16out":
-            fq.fp8q_gemm_bf16(A, W, Cb)
         elif name == "fp8q_gemm":
             fq.fp8q_gemm(aq, as_, wq, ws, C)
         else:  # hipBLASLt through torch, BF16 out
@@ -160,7 +158,6 @@ def setup_bf16(fq, torch, sets):
     flops = 2.0 * M * N * K
     kernels = [
         ("fp8q_gemm_bf16", "mfma_bf16", flops, "flop"),
-        ("fp8q_gemm_bf16_bf16out", "mfma_bf16", flops, "flop"),
         ("torch_matmul_bf16_hipblaslt", "mfma_bf16", flops, "flop"),
         ("fp8q_gemm", "mfma", flops, "flop"),
     ]

@@ -214,3 +214,35 @@ def test_per_tensor_quantizer_outlier_sensitivity():
     rel_f = (err_f[small] / np.abs(x[small])).mean()
     rel_t = (err_t[small] / np.abs(x[small])).mean()
     assert rel_f <= 2.0 ** -4 and rel_t > 3 * rel_f
+
+
+def test_outlier_study_gemm_error_fine_grained_vs_per_tensor():
+    """GEMM-level outlier sensitivity (an accuracy study; the pages print no
+    magnitudes, so the numbers are parity unpinned and only their order is
+    asserted).  Dense-workload rows (64 rows x 1024 weight rows, K = 7168) with
+    its 72 outlier K-channels scaled by c; errors of the exact products of the
+    dequantized operands against the exact BF16 product, in units of
+    sum_k |a_k||w_k|, weights always 128x128-block quantized.  Without outliers
+    one scale per tensor is as good as 1x128 groups; with them the per-tensor
+    activation scale is worse by a quarter or more."""
+    from oracle import gemm
+    c = workloads.WORKLOADS["dense"]
+    K = c["K"]
+    outl = workloads.outlier_channels(K, c["seed"], c["outlier_frac"], c["outlier_count"])
+    W = workloads.weight_rows(np.arange(1024), K, c["seed"], c["w_std"])
+    qw, sw = quant.quantize_weight(W)
+    Wd = quant.dequantize_weight(qw, sw)
+    ratio = {}
+    for mult in (1.0, 30.0, 300.0):
+        A = workloads.act_rows(np.arange(64), K, c["seed"], c["act_std"], outl, mult)
+        ref = gemm.gemm_bf16(A, W)
+        absb = gemm.abs_bound_bf16(A, W)
+        qa, sa = quant.quantize_act(A)
+        ef = np.median(np.abs(quant.dequantize_act(qa, sa) @ Wd.T - ref) / absb)
+        qt, st = quant.quantize_tensor(A)
+        et = np.median(np.abs((e4m3.decode(qt) * float(st)) @ Wd.T - ref) / absb)
+        ratio[mult] = et / ef
+        print(f"outliers x{mult:g}: fine {ef:.3e} per-tensor {et:.3e} ratio {et / ef:.2f}")
+        assert ef < 2e-3 if mult <= 30 else ef < 5e-3
+    assert abs(ratio[1.0] - 1.0) < 0.03
+    assert ratio[30.0] > 1.15 and ratio[300.0] > 1.2
