@@ -79,6 +79,28 @@ def grouped_gemm(qa, sa, offsets, qw, sw):
     return C
 
 
+def gemm_rowscaled(qa, sa, qb, sb):
+    """Block-scaled GEMM whose both operands carry 1x128 row-group scales (the
+    weight-gradient GEMM, dW = dY^T X: operands dY^T and X^T grouped along the
+    tokens; [goodkr-2169793], mixed-precision framework passage):
+
+        C[m][n] = sum_g (sa[g][m] * sb[g][n]) * P_g[m][n]
+
+    qa: uint8[M][K], sa: float32[K/128][M], qb: uint8[N][K], sb: float32[K/128][N].
+    """
+    M, K = qa.shape
+    N = qb.shape[0]
+    C = np.zeros((M, N), dtype=np.float64)
+    for g, P in chunk_partials(qa, qb):
+        C += (sa[g].astype(np.float64)[:, None] * sb[g].astype(np.float64)[None, :]) * P
+    return C
+
+
+def abs_bound_rowscaled(qa, sa, qb, sb):
+    """sum_k |dec(qa) s_a| * |dec(qb) s_b| per output (float64[M][N])."""
+    return gemm_rowscaled(qa & np.uint8(0x7F), np.abs(sa), qb & np.uint8(0x7F), np.abs(sb))
+
+
 def gemm_bf16(a_bits, w_bits):
     """BF16 reference GEMM: C (float64[M][N]) = sum_k a[m][k] * w[n][k].
 

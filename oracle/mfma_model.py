@@ -101,6 +101,19 @@ def gemm(qa, sa, qw, sw):
     return C
 
 
+def gemm_rowscaled(qa, sa, qb, sb):
+    """The same with 1x128 row-group scales on both operands:
+    C = sum_g (s_a[g][m] * s_b[g][n]) * P_model_g[m][n], sb: float32[K/128][N]."""
+    M = qa.shape[0]
+    N = qb.shape[0]
+    C = np.zeros((M, N), dtype=np.float64)
+    sbf = sb.astype(np.float64)                        # [G][N]
+    for m in range(M):
+        P = group_partials(qa[m], qb)                  # [G][N]
+        C[m] = (sa[:, m].astype(np.float64)[:, None] * sbf * P).sum(axis=0)
+    return C
+
+
 def fp32_rounding_bound(qa, sa, qw, sw, abs_bound):
     """Bound on |C_gpu - C_model| from FP32 rounding alone.
 

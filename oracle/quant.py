@@ -132,6 +132,33 @@ def quantize_weight(w_bits, mode="f32"):
     return q, s.astype(np.float32)
 
 
+def quantize_act_t(x_bits, mode="f32"):
+    """Transposed activation quantization for the weight-gradient GEMM, whose
+    inner dimension is the token dimension M ([goodkr-2169793], mixed-precision
+    framework passage: Fprop, Dgrad and Wgrad all run in FP8; the scales are
+    per group along each GEMM's inner dimension).  Groups are 128 consecutive
+    rows of one column: the 1x128 rule applied to x^T.
+
+    x_bits: uint16[M][K], M % 128 == 0.
+    Returns q_t: uint8[K][M] (codes of x^T), s_t: float32[M/128][K].
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    if x_bits.shape[0] % GROUP:
+        raise ValueError("M must be a multiple of 128")
+    return quantize_act(np.ascontiguousarray(x_bits.T), mode)
+
+
+def quantize_weight_t(w_bits, mode="f32"):
+    """Transposed weight quantization for the activation-gradient GEMM
+    (dX = dY W uses W^T as its weight operand): the 128x128 block rule applied
+    to w^T, i.e. the same blocks with their codes transposed.
+
+    w_bits: uint16[N][K].  Returns q_t: uint8[K][N], s_t: float32[K/128][N/128].
+    """
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    return quantize_weight(np.ascontiguousarray(w_bits.T), mode)
+
+
 def dequantize_act(q, s):
     """dec(q) * s as float64[M][K] (s laid out [K/128][M])."""
     v = e4m3.decode(q)

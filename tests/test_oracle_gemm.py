@@ -175,3 +175,52 @@ def test_bf16_reference_permutation_picks_columns():
     w[np.arange(N), p] = 1.0
     C = gemm.gemm_bf16(a, workloads.bf16_bits(w))
     assert np.array_equal(C, quant.bf16_bits_to_f32(a)[:, p].astype(np.float64))
+
+
+def test_rowscaled_gemm_exact_and_reduces_to_block_scaled():
+    """gemm_rowscaled: exact rational brute force on a tiny case, and equal to
+    gemm() when the second operand's row scales are constant over 128-row
+    blocks (sb[g][n] = sw[n // 128][g])."""
+    rng = np.random.default_rng(12)
+    M, N, K = 4, 256, 384
+    A = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    B = workloads.bf16_bits(rng.standard_normal((N, K)).astype(np.float32))
+    qa, sa = quant.quantize_act(A)
+    qb, sb = quant.quantize_act(B)     # row-group scales [K/128][N]
+    C = gemm.gemm_rowscaled(qa, sa, qb, sb)
+    bound = gemm.abs_bound_rowscaled(qa, sa, qb, sb)
+    dec = [Fraction(float(v)) if np.isfinite(v) else None for v in e4m3.DECODE_TABLE]
+    for m in range(M):
+        for n in (0, 3, 129, 255):
+            exact = sum(Fraction(float(sa[k // 128, m])) * Fraction(float(sb[k // 128, n]))
+                        * dec[qa[m, k]] * dec[qb[n, k]] for k in range(K))
+            assert abs(Fraction(float(C[m, n])) - exact) <= Fraction(float(bound[m, n])) * Fraction(4, 2**53)
+    qw, sw = quant.quantize_weight(workloads.bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32)))
+    sb_blocks = np.repeat(sw, 128, axis=0).T.copy()  # [K/128][N]
+    assert np.array_equal(gemm.gemm_rowscaled(qa, sa, qw, sb_blocks), gemm.gemm(qa, sa, qw, sw))
+
+
+def test_backward_gemms_of_a_linear_layer():
+    """Dgrad and Wgrad of Y = X W^T through the quantized operands agree with
+    the float64 gradients to within the FP8 quantization error: a check that
+    the operands and their transposes are wired the right way round."""
+    rng = np.random.default_rng(13)
+    M, N, K = 256, 256, 384
+    X = workloads.bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    W = workloads.bf16_bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    dY = workloads.bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    Xf, Wf, dYf = (quant.bf16_bits_to_f32(t).astype(np.float64) for t in (X, W, dY))
+    # Dgrad: dX = dY W  (inner dimension N)
+    qd, sd = quant.quantize_act(dY)
+    qwt, swt = quant.quantize_weight_t(W)
+    dX = gemm.gemm(qd, sd, qwt, swt)
+    ref = dYf @ Wf
+    assert np.linalg.norm(dX - ref) / np.linalg.norm(ref) < 0.06
+    # Wgrad: dW = dY^T X  (inner dimension M, both operands grouped along M)
+    qa, sa = quant.quantize_act_t(dY)   # dY^T [N][M]
+    qb, sb = quant.quantize_act_t(X)    # X^T  [K][M]
+    dW = gemm.gemm_rowscaled(qa, sa, qb, sb)
+    refw = dYf.T @ Xf
+    assert np.linalg.norm(dW - refw) / np.linalg.norm(refw) < 0.06
+    # a transposed operand would be far off
+    assert np.linalg.norm(dW.T[:N, :N] - refw[:N, :N]) / np.linalg.norm(refw[:N, :N]) > 0.5

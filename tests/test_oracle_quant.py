@@ -246,3 +246,35 @@ def test_outlier_study_gemm_error_fine_grained_vs_per_tensor():
         assert ef < 2e-3 if mult <= 30 else ef < 5e-3
     assert abs(ratio[1.0] - 1.0) < 0.03
     assert ratio[30.0] > 1.15 and ratio[300.0] > 1.2
+
+
+def test_transposed_quantizers_are_the_rules_on_the_transpose():
+    """quantize_act_t groups 128 consecutive rows of a column (its codes and
+    scales equal a column-by-column evaluation of the 1x128 rule written out
+    here); quantize_weight_t is quantize_weight with every block transposed."""
+    rng = np.random.default_rng(9)
+    M, K = 256, 384
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, 5] *= 40
+    x[130, :] = 0
+    xb = workloads.bf16_bits(x)
+    qt, st = quant.quantize_act_t(xb)
+    assert qt.shape == (K, M) and st.shape == (M // 128, K)
+    xv = quant.bf16_bits_to_f32(xb)
+    for k in (0, 5, 200, K - 1):
+        for g in range(M // 128):
+            col = xv[g * 128:(g + 1) * 128, k]
+            amax = np.float32(np.abs(col).max())
+            inv = np.float32(448.0) / amax
+            assert st[g, k] == np.float32(amax / np.float32(448.0))
+            want = e4m3.encode((col * inv).astype(np.float32))
+            assert np.array_equal(qt[k, g * 128:(g + 1) * 128], want)
+    # weights: the same 128x128 blocks, transposed
+    w = workloads.bf16_bits((rng.standard_normal((256, 384)) * 0.02).astype(np.float32))
+    q, s = quant.quantize_weight(w)
+    qwt, swt = quant.quantize_weight_t(w)
+    assert np.array_equal(qwt, q.T) and np.array_equal(swt, s.T)
+    for mode in ("f32", "pow2"):
+        q2, s2 = quant.quantize_weight(w, mode)
+        q3, s3 = quant.quantize_weight_t(w, mode)
+        assert np.array_equal(q3, q2.T) and np.array_equal(s3, s2.T)
