@@ -39,6 +39,12 @@ lib.fp8q_gemm.restype = _st
 lib.fp8q_grouped_gemm.argtypes = [_p, _p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32, _p]
 lib.fp8q_grouped_gemm.restype = _st
 lib.fp8q_gemm_bf16.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i32, _p]
+lib.fp8q_quantize_act_t.argtypes = [_p, _i64, _i64, _p, _p, _i32, _p]
+lib.fp8q_quantize_act_t.restype = _st
+lib.fp8q_quantize_weight_t.argtypes = [_p, _i64, _i64, _p, _p, _i32, _p]
+lib.fp8q_quantize_weight_t.restype = _st
+lib.fp8q_gemm_rowscaled.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
+lib.fp8q_gemm_rowscaled.restype = _st
 lib.fp8q_gemm_bf16.restype = _st
 lib.fp8q_status_string.argtypes = [_st]
 lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -127,6 +133,30 @@ def fp8q_gemm_bf16(a, w, c, stream=None):
            "fp8q_gemm_bf16")
 
 
+def fp8q_quantize_act_t(x, q_t, s_t, mode="f32", stream=None):
+    """x: bf16 [M][K] -> q_t: uint8 [K][M], s_t: float32 [M/128][K] (in place)."""
+    M, K = x.shape
+    _check(lib.fp8q_quantize_act_t(_ptr(x), M, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
+                                   _stream(stream, x.device)), "fp8q_quantize_act_t")
+
+
+def fp8q_quantize_weight_t(w, q_t, s_t, mode="f32", stream=None):
+    """w: bf16 [N][K] -> q_t: uint8 [K][N], s_t: float32 [K/128][N/128] (in place)."""
+    N, K = w.shape
+    _check(lib.fp8q_quantize_weight_t(_ptr(w), N, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
+                                      _stream(stream, w.device)), "fp8q_quantize_weight_t")
+
+
+def fp8q_gemm_rowscaled(a_q, a_s, b_q, b_s, c, stream=None):
+    """c[M][N] = a_q[M][K] x b_q[N][K]^T with 1x128 row-group scales on both."""
+    import torch
+    M, K = a_q.shape
+    N = b_q.shape[0]
+    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    _check(lib.fp8q_gemm_rowscaled(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K, _ptr(c),
+                                   out, _stream(stream, a_q.device)), "fp8q_gemm_rowscaled")
+
+
 # ---------------------------------------------------------- allocation helpers
 def quantize_act(x, mode="f32", stream=None):
     import torch
@@ -144,6 +174,32 @@ def quantize_weight(w, mode="f32", stream=None):
     s = torch.empty((N // GROUP, K // GROUP), dtype=torch.float32, device=w.device)
     fp8q_quantize_weight(w, q, s, mode, stream)
     return q, s
+
+
+def quantize_act_t(x, mode="f32", stream=None):
+    import torch
+    M, K = x.shape
+    q = torch.empty((K, M), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M // GROUP, K), dtype=torch.float32, device=x.device)
+    fp8q_quantize_act_t(x, q, s, mode, stream)
+    return q, s
+
+
+def quantize_weight_t(w, mode="f32", stream=None):
+    import torch
+    N, K = w.shape
+    q = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+    s = torch.empty((K // GROUP, N // GROUP), dtype=torch.float32, device=w.device)
+    fp8q_quantize_weight_t(w, q, s, mode, stream)
+    return q, s
+
+
+def gemm_rowscaled(a_q, a_s, b_q, b_s, out_dtype=None, stream=None):
+    import torch
+    out_dtype = out_dtype or torch.float32
+    c = torch.empty((a_q.shape[0], b_q.shape[0]), dtype=out_dtype, device=a_q.device)
+    fp8q_gemm_rowscaled(a_q, a_s, b_q, b_s, c, stream)
+    return c
 
 
 def gemm(a_q, a_s, w_q, w_s, out_dtype=None, stream=None):

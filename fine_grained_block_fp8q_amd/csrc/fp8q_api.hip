@@ -24,6 +24,13 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
                                int64_t N, int64_t K, void* c, int out_bf16, hipStream_t stream);
 hipError_t launch_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
                             void* c, int out_bf16, hipStream_t stream);
+hipError_t launch_quantize_act_t(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                 int mode, hipStream_t stream);
+hipError_t launch_quantize_weight_t(const void* w, int64_t N, int64_t K, uint8_t* qt,
+                                    float* st, int mode, hipStream_t stream);
+hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                 const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                 int out_bf16, hipStream_t stream);
 }  // namespace fp8q
 
 namespace {
@@ -166,6 +173,52 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c,
                                             out == FP8Q_OUT_BF16, stream));
+}
+
+fp8q_status fp8q_quantize_act_t(const void* x_bf16, int64_t M, int64_t K, uint8_t* q_t,
+                                float* s_t, fp8q_scale_mode mode, hipStream_t stream) {
+  const bool empty = (M == 0 || K == 0);
+  if (!empty && (!x_bf16 || !q_t || !s_t)) return FP8Q_ERR_NULL;
+  if (M < 0 || K < 0 || M % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(q_t, 16) || !aligned(s_t, 4)) return FP8Q_ERR_ALIGN;
+  if (!valid_mode(mode)) return FP8Q_ERR_ENUM;
+  if (empty) return FP8Q_OK;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_quantize_act_t(x_bf16, M, K, q_t, s_t, (int)mode, stream));
+}
+
+fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, uint8_t* q_t,
+                                   float* s_t, fp8q_scale_mode mode, hipStream_t stream) {
+  const bool empty = (N == 0 || K == 0);
+  if (!empty && (!w_bf16 || !q_t || !s_t)) return FP8Q_ERR_NULL;
+  if (N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(q_t, 16) || !aligned(s_t, 4)) return FP8Q_ERR_ALIGN;
+  if (!valid_mode(mode)) return FP8Q_ERR_ENUM;
+  if (empty) return FP8Q_OK;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_quantize_weight_t(w_bf16, N, K, q_t, s_t, (int)mode, stream));
+}
+
+fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                fp8q_out_dtype out, hipStream_t stream) {
+  const bool empty_out = (M == 0 || N == 0);
+  if (!empty_out && !c) return FP8Q_ERR_NULL;
+  if (!empty_out && K != 0 && (!a_q || !a_s || !b_q || !b_s)) return FP8Q_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(a_q, 16) || !aligned(b_q, 16) || !aligned(c, 16) || !aligned(a_s, 4) ||
+      !aligned(b_s, 4))
+    return FP8Q_ERR_ALIGN;
+  if (!valid_out(out)) return FP8Q_ERR_ENUM;
+  if (empty_out) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_UNSUPPORTED;
+  if (!gemm_extent_ok(M, K) || !gemm_extent_ok(N, K)) return FP8Q_ERR_UNSUPPORTED;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_gemm_rowscaled(a_q, a_s, b_q, b_s, M, N, K, c,
+                                              out == FP8Q_OUT_BF16, stream));
 }
 
 fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,

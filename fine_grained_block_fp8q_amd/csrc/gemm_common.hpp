@@ -44,6 +44,7 @@ struct TileArgs {
   int64_t w_rows;       // N
   int64_t K;
   int64_t sa_ld;        // leading dimension of SA (total rows)
+  int64_t sw_ld;        // row-scaled weight operand: leading dimension of SW = [K/128][sw_ld]
   void* C;              // output base
   int64_t ldc;          // N
   int out_bf16;

@@ -40,10 +40,15 @@ namespace fp8q {
 // a 128-byte stage row then holds 64 K values, each 16x16 block takes two
 // chained 16x16x32 BF16 MFMAs per chunk, accumulating in the matrix core (its
 // BF16 path accumulates to FP32 accuracy), and there are no scales.
+// W_ROWSCALE_: the weight-side operand carries 1x128 row-group scales
+// ([K/128][N], like the activations) instead of 128x128 block scales: the
+// weight-gradient GEMM, whose operands dY^T and X^T are both grouped along
+// the tokens.  The multiplier then differs per output element.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int ROWS_ = BM_,
-          int PF_ = 0, int OP_BF16_ = 0>
+          int PF_ = 0, int OP_BF16_ = 0, int W_ROWSCALE_ = 0>
 struct GemmCfg {
   static constexpr bool OP_BF16 = OP_BF16_ != 0;
+  static constexpr bool W_ROWSCALE = W_ROWSCALE_ != 0;
   static constexpr int SUB = OP_BF16 ? 2 : 1;       // MFMAs per 16x16 block per chunk
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -60,7 +65,8 @@ struct GemmCfg {
   static constexpr int A_BYTES = ROWS * BK;
   static constexpr int B_BYTES = BN * BK;
   static constexpr int SA_BYTES = OP_BF16 ? 0 : WAVES_M * 256;  // 64 row scales per row of waves
-  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
+  static constexpr int SB_BYTES = W_ROWSCALE ? BN * 4 : 0;        // the tile's weight-row scales
+  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
   static constexpr int PF_BYTES = PF_LOADS > 0 ? NWAVES * 256 : 0;  // their LDS landing slots
@@ -69,7 +75,7 @@ struct GemmCfg {
   static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
   static constexpr int PER_WAVE = (OP_BLK + NWAVES - 1) / NWAVES;  // operand loads per wave
   static constexpr int PAD = PER_WAVE * NWAVES - OP_BLK;  // repeated A loads that even them out
-  static constexpr int LOADS = PER_WAVE + (OP_BF16 ? 0 : 1);  // + the scale slot
+  static constexpr int LOADS = PER_WAVE + (OP_BF16 ? 0 : 1) + (W_ROWSCALE ? 1 : 0);  // + scales
   static_assert(WM % 16 == 0 && WM <= 64, "a wave's rows fit one 256-byte scale slot");
   static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
   // Staged rows: whole 1 KiB loads.  When they stop inside a wave (160 rows
@@ -82,6 +88,8 @@ struct GemmCfg {
   static_assert(PF_LOADS == 0 || (PF_LOADS == 1 && NWAVES >= 2 && ROWS == 256 && BN == 256),
                 "the prefetch share is laid out for 256 x 256 tiles");
   static_assert(LOADS * (STAGES - 1) + PF_LOADS * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(!W_ROWSCALE || (!OP_BF16 && NWAVES == 8 && BN == 256 && WN == 128),
+                "row-scaled weights: 8 waves, each loading 64 of the 256 row scales");
 };
 
 // Dense configuration: 256 x 256 tiles, 8 waves (two per SIMD, so one wave's
@@ -91,6 +99,8 @@ struct GemmCfg {
 using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 // The BF16 GEMM: the same tile, waves, ring and prefetch.
 using DenseBf16Cfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 1>;
+// The weight-gradient GEMM: the dense tile with row-scaled weights.
+using RowScaledCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 0, 1>;
 // Grouped configurations: 256-row tiles cover an expert's tokens (decode
 // batches hold at most 256) so each expert's weights stream once, and 256
 // weight rows per tile (8 waves of 64 x 128, as in the dense tile) so each
@@ -147,9 +157,11 @@ constexpr int kBarLead = 2;
 // chunk's K offset as the scalar soffset, so issuing a load costs no VALU.
 template <class Cfg>
 struct ChunkLoader {
-  __amdgpu_buffer_rsrc_t ra, rw, rs;
+  __amdgpu_buffer_rsrc_t ra, rw, rs, rsb;
   uint32_t voff[Cfg::PER_WAVE];
   uint32_t voff_s;
+  uint32_t voff_sb;   // this lane's weight-row scale (row-scaled weights)
+  int64_t sb_stride;  // bytes between consecutive chunks' weight-row scales
   uint32_t voff_pf;  // this lane's L2 prefetch line (first byte of its K chunk)
   bool pf_a;         // the wave prefetches A rows (else W rows)
   int64_t s_stride;  // bytes between consecutive chunks' row scales
@@ -191,6 +203,15 @@ struct ChunkLoader {
       const int64_t rs_row = wave_m_ * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
       voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
     }
+    if constexpr (Cfg::W_ROWSCALE) {
+      // Wave w loads the scales of weight rows 64*(w%4) .. +63 of the tile
+      // (waves w and w+4 write the same values).
+      const int64_t G = t.K / Cfg::BK;
+      rsb = make_rsrc(t.SW + t.w_row0, (G * t.sw_ld - t.w_row0) * 4);
+      sb_stride = t.sw_ld * 4;
+      const int64_t sb_row = (wave_ % 4) * 64 + lane;
+      voff_sb = (uint32_t)((sb_row < w_live ? sb_row : w_live - 1) * 4);
+    }
     // L2 prefetch lines.  The XCD-aware tile order gives one XCD a block of
     // 4 tile rows x 8 tile columns, so 8 tiles share each 256-row A band and
     // 4 share each W band in that XCD's L2.  A tile therefore prefetches
@@ -222,10 +243,15 @@ struct ChunkLoader {
       const int dst = is_a ? m * 1024 : Cfg::A_BYTES + (m - Cfg::A_BLK) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rw, to_lds(stage + dst), 16, voff[d],
                                                (int)(g * Cfg::BK), 0, 0);
-    } else if constexpr (!Cfg::OP_BF16) {
+    } else if (!Cfg::OP_BF16 && d == Cfg::PER_WAVE) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256), 4, voff_s,
           (int)(g * s_stride), 0, 0);
+    } else if constexpr (Cfg::W_ROWSCALE) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb,
+          to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::SA_BYTES + (wave % 4) * 256), 4,
+          voff_sb, (int)(g * sb_stride), 0, 0);
     }
   }
 };
@@ -240,6 +266,15 @@ __device__ __forceinline__ v4f mfma_bf16_half(const v8i& w, const v8i& a, const 
   const v4i ah = h ? v4i{a[4], a[5], a[6], a[7]} : v4i{a[0], a[1], a[2], a[3]};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, wh),
                                                  __builtin_bit_cast(v8bf, ah), acc, 0, 0, 0);
+}
+
+// Promotion with row-scaled weights: acc += P * (s_a[row] * s_b[col]), the
+// lane's 4 results having 4 weight rows.
+__device__ __forceinline__ void promote_rows(v4f& acc, const v4f& p, float sa, const v4f& sb) {
+  acc[0] = __builtin_fmaf(p[0], sa * sb[0], acc[0]);
+  acc[1] = __builtin_fmaf(p[1], sa * sb[1], acc[1]);
+  acc[2] = __builtin_fmaf(p[2], sa * sb[2], acc[2]);
+  acc[3] = __builtin_fmaf(p[3], sa * sb[3], acc[3]);
 }
 
 // Promotion of one 16x16 chunk partial: acc += P * (s_a[row] * s_w).
@@ -266,7 +301,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
 
   // Weight-scale row of this wave's weight rows (one 128-row block).
   const float* sw_row = nullptr;
-  if constexpr (!Cfg::OP_BF16) {
+  if constexpr (!Cfg::OP_BF16 && !Cfg::W_ROWSCALE) {
     int64_t wblk = (t.w_row0 + wave_n * Cfg::WN) / 128;
     const int64_t last_wblk = t.w_rows / 128 - 1;
     wblk = wblk < last_wblk ? wblk : last_wblk;
@@ -393,13 +428,24 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
 
     const uint8_t* Bs = st_cur + Cfg::A_BYTES;
     float mult[MB];
+    v4f sa;
+    // Row-scaled weights: the scales of row block j (this lane's 4 weight
+    // rows) go into a 3-slot ring when the block's fragment is prefetched;
+    // its last promotion comes before the slot is reused.
+    const float* SBs =
+        reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::SA_BYTES);
+    v4f sbv[3];
     if constexpr (!Cfg::OP_BF16) {
       const float* SAs =
           reinterpret_cast<const float*>(st_cur + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256);
-      const float sw = sw_row[g];
-      const v4f sa = *reinterpret_cast<const v4f*>(SAs + 4 * r16);
+      sa = *reinterpret_cast<const v4f*>(SAs + 4 * r16);
+      if constexpr (Cfg::W_ROWSCALE) {
+        sbv[0] = *reinterpret_cast<const v4f*>(SBs + wave_n * Cfg::WN + 4 * q);
+      } else {
+        const float sw = sw_row[g];
 #pragma unroll
-      for (int i = 0; i < MB; ++i) mult[i] = sa[i] * sw;
+        for (int i = 0; i < MB; ++i) mult[i] = sa[i] * sw;
+      }
     }
     v4f p[LAG + 1];
 #pragma unroll
@@ -408,6 +454,12 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
         const int i = k % MB, h = (k / MB) % Cfg::SUB, j = k / RB;
         if (k % RB == 0 && j + BPF < NB)
           b[(j + BPF) % NBUF] = load_frag(Bs, wave_n * Cfg::WN + (j + BPF) * 16 + r16, q);
+        if constexpr (Cfg::W_ROWSCALE) {
+          static_assert(RB * (NB - 2) < kBar, "row scales are read before the barrier");
+          if (k % RB == 0 && j + 1 < NB)
+            sbv[(j + 1) % 3] =
+                *reinterpret_cast<const v4f*>(SBs + wave_n * Cfg::WN + (j + 1) * 16 + 4 * q);
+        }
         if constexpr (Cfg::OP_BF16) {
           acc[i][j] = mfma_bf16_half(b[j % NBUF], a[i], acc[i][j], h);
         } else {
@@ -446,7 +498,11 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
       // MFMA (to hand its result registers to MFMA k), which leaves it right
       // behind MFMA k-LAG+1 and stalls the wave on the matrix core's result.
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!Cfg::OP_BF16) {
+      if constexpr (Cfg::W_ROWSCALE) {
+        const int kp = k - LAG;
+        if (kp >= 0)
+          promote_rows(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], sa[kp % MB], sbv[(kp / MB) % 3]);
+      } else if constexpr (!Cfg::OP_BF16) {
         const int kp = k - LAG;
         if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
       }
@@ -498,6 +554,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void gemm_kernel(
   t.w_rows = N;
   t.K = K;
   t.sa_ld = M;
+  t.sw_ld = N;
   t.C = C;
   t.ldc = N;
   t.out_bf16 = out_bf16;
@@ -672,6 +729,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
     t.w_rows = N;
     t.K = K;
     t.sa_ld = M_total;
+    t.sw_ld = N;
     t.C = C;
     t.ldc = N;
     t.out_bf16 = out_bf16;
@@ -702,6 +760,20 @@ hipError_t launch_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, 
   hipLaunchKernelGGL(gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream,
                      static_cast<const uint8_t*>(a), nullptr, static_cast<const uint8_t*>(w),
                      nullptr, M, N, 2 * K, c, out_bf16, (int)tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                 const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                 int out_bf16, hipStream_t stream) {
+  using Cfg = RowScaledCfg;
+  if (M == 0 || N == 0) return hipSuccess;
+  const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+  const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream, a_q,
+                     a_s, b_q, b_s, M, N, K, c, out_bf16, (int)tiles_n);
   return hipGetLastError();
 }
 

@@ -197,6 +197,153 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(
   (void)N;
 }
 
+// ---------------------------------------------------------------------------
+// Transposed quantizers for the backward GEMMs.  The weight-gradient GEMM
+// (dW = dY^T X) contracts over the tokens, so its operands dY^T and X^T are
+// quantized in groups of 128 consecutive rows of one column of dY and X; the
+// activation-gradient GEMM (dX = dY W) takes W^T, whose 128x128 blocks are
+// those of W with their codes transposed.  Both kernels write the codes of
+// the transposed matrix directly.
+
+// BF16 element j (0..7) of a 16-byte load, as float.
+__device__ __forceinline__ float bf16_at(const uint4& v, int j) {
+  const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+__device__ __forceinline__ void store_code_word(uint8_t* dst, uint32_t w) {
+  __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(dst));
+}
+
+// Activations, transposed: x[M][K] -> q_t[K][M], s_t[M/128][K].  A workgroup
+// covers 128 rows (one group of tokens) x 64 columns.  Lane (rq = t/8,
+// cp = t%8) loads rows 4rq .. 4rq+3 at columns 8cp .. 8cp+7, so 8 lanes read a
+// row's 128 contiguous bytes.  A column's max-abs is reduced over the lane's
+// 4 rows, across the 8 lanes of the wave that share cp (shuffles), then
+// across the 4 waves through LDS.  The lane packs the codes of its 4
+// consecutive rows of each column into one word of that column's output row:
+// the 8 lanes of a wave with equal cp write 32 contiguous bytes of it, and the
+// 4 waves the whole 128.
+template <int MODE>
+__global__ __launch_bounds__(256) void quantize_act_t_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, uint8_t* __restrict__ qt,
+    float* __restrict__ st, int64_t n_kblk) {
+  __shared__ float red[4][64];
+  const int64_t bid = blockIdx.x;
+  const int64_t kb = bid % n_kblk;  // 64-column block (fastest: neighbours share rows)
+  const int64_t mb = bid / n_kblk;  // group of 128 rows
+  const int t = threadIdx.x;
+  const int rq = t >> 3, cp = t & 7;
+  const int wave = t >> 6;
+  const int64_t m0 = mb * kGroup + 4 * rq;
+  const int64_t k0 = kb * 64 + 8 * cp;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (m0 + i) * K + k0);
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = fmaxf(fmaxf(fabsf(bf16_at(v[0], j)), fabsf(bf16_at(v[1], j))),
+                 fmaxf(fabsf(bf16_at(v[2], j)), fabsf(bf16_at(v[3], j))));
+#pragma unroll
+    for (int d = 8; d < 64; d <<= 1) a[j] = fmaxf(a[j], __shfl_xor(a[j], d));
+  }
+  if ((t & 63) < 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[wave][8 * cp + j] = a[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 8 * cp + j;
+    const float amax = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+    const GroupRule r = group_rule<MODE>(amax);
+    if (rq == 0) st[mb * K + k0 + j] = r.s;
+    const uint32_t w = pack_e4m3x4(apply<MODE>(bf16_at(v[0], j), r), apply<MODE>(bf16_at(v[1], j), r),
+                                   apply<MODE>(bf16_at(v[2], j), r), apply<MODE>(bf16_at(v[3], j), r));
+    store_code_word(qt + (k0 + j) * M + m0, w);
+  }
+}
+
+// Weights, transposed: w[N][K] -> q_t[K][N], s_t[K/128][N/128].  One 256-lane
+// workgroup per 128x128 block: lane (rq = t/16, cp = t%16) loads rows
+// 8rq .. 8rq+7 at columns 8cp .. 8cp+7 (16 lanes read a row's 256 bytes).
+// The block max is reduced as in quantize_weight_kernel (each DPP row is one
+// rq); each lane then writes 8 bytes, its 8 consecutive rows, of each of its 8
+// columns' output rows.
+template <int MODE>
+__global__ __launch_bounds__(256) void quantize_weight_t_kernel(
+    const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ qt,
+    float* __restrict__ st, int64_t KB) {
+  __shared__ float red[4];
+  const int64_t bid = blockIdx.x;
+  const int64_t nb = bid / KB;
+  const int64_t kb = bid % KB;
+  const int t = threadIdx.x;
+  const int rq = t >> 4, cp = t & 15;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int64_t n0 = nb * kGroup + 8 * rq;
+  const int64_t k0 = kb * kGroup + 8 * cp;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(w + (n0 + i) * K + k0);
+  float a = absmax8(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) a = fmaxf(a, absmax8(v[i]));
+  a = row16_max(a);
+  a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16))),
+            fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)),
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48))));
+  if (lane == 0) red[wave] = a;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const GroupRule r = group_rule<MODE>(amax);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint2 o;
+    o.x = pack_e4m3x4(apply<MODE>(bf16_at(v[0], j), r), apply<MODE>(bf16_at(v[1], j), r),
+                      apply<MODE>(bf16_at(v[2], j), r), apply<MODE>(bf16_at(v[3], j), r));
+    o.y = pack_e4m3x4(apply<MODE>(bf16_at(v[4], j), r), apply<MODE>(bf16_at(v[5], j), r),
+                      apply<MODE>(bf16_at(v[6], j), r), apply<MODE>(bf16_at(v[7], j), r));
+    store_codes(qt + (k0 + j) * N + n0, o);
+  }
+  if (t == 0) st[kb * (N / kGroup) + nb] = r.s;
+}
+
+hipError_t launch_quantize_act_t(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                 int mode, hipStream_t stream) {
+  const int64_t n_kblk = K / 64;
+  const int64_t blocks = (M / kGroup) * n_kblk;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL(quantize_act_t_kernel<0>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), M, K, qt, st, n_kblk);
+  else
+    hipLaunchKernelGGL(quantize_act_t_kernel<1>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(x), M, K, qt, st, n_kblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight_t(const void* w, int64_t N, int64_t K, uint8_t* qt,
+                                    float* st, int mode, hipStream_t stream) {
+  const int64_t KB = K / kGroup;
+  const int64_t blocks = (N / kGroup) * KB;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (mode == 0)
+    hipLaunchKernelGGL(quantize_weight_t_kernel<0>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), N, K, qt, st, KB);
+  else
+    hipLaunchKernelGGL(quantize_weight_t_kernel<1>, grid, block, 0, stream,
+                       static_cast<const uint16_t*>(w), N, K, qt, st, KB);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_act(const void* x, int64_t M, int64_t K, uint8_t* q, float* s,
                                int mode, hipStream_t stream) {
   const int64_t G = K / kGroup;

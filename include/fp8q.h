@@ -150,6 +150,54 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
                               void* c, fp8q_out_dtype out, hipStream_t stream);
 
 /*
+ * Backward GEMMs (the-good.kr post 2169793, mixed-precision framework
+ * passage: Fprop, Dgrad and Wgrad of a linear layer all run in FP8; scales
+ * are per group along each GEMM's inner dimension).  For Y = X W^T:
+ *   Dgrad  dX = dY W     : fp8q_gemm(fp8q_quantize_act(dY), fp8q_quantize_weight_t(W))
+ *   Wgrad  dW = dY^T X   : fp8q_gemm_rowscaled(fp8q_quantize_act_t(dY), fp8q_quantize_act_t(X))
+ *
+ * Transposed activation quantization: groups of 128 consecutive rows (tokens)
+ * of one column, the 1x128 rule of fp8q_quantize_act applied to x^T.
+ *   x_bf16 : [M][K] bfloat16, row-major; 16-byte aligned.
+ *   q_t    : [K][M] uint8 E4M3 codes of x^T (output); 16-byte aligned.
+ *   s_t    : [M/128][K] float32 (output): s_t[g][k] scales rows 128g..128g+127
+ *            of column k (the activation-scale layout of an operand with K rows).
+ *   M % 128 == 0, K % 128 == 0.
+ */
+fp8q_status fp8q_quantize_act_t(const void* x_bf16, int64_t M, int64_t K,
+                                uint8_t* q_t, float* s_t, fp8q_scale_mode mode,
+                                hipStream_t stream);
+
+/*
+ * Transposed weight quantization: the 128x128 blocks of fp8q_quantize_weight
+ * with their codes written transposed, i.e. the weight operand W^T of Dgrad.
+ *   w_bf16 : [N][K] bfloat16, row-major; 16-byte aligned.
+ *   q_t    : [K][N] uint8 E4M3 codes of w^T (output); 16-byte aligned.
+ *   s_t    : [K/128][N/128] float32 (output; the transpose of the block scales).
+ *   N % 128 == 0, K % 128 == 0.
+ */
+fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K,
+                                   uint8_t* q_t, float* s_t, fp8q_scale_mode mode,
+                                   hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM whose both operands carry 1x128 row-group scales
+ * (the weight-gradient GEMM; promotion every 128 K as in fp8q_gemm):
+ *   C[m][n] = sum_g (a_s[g][m] * b_s[g][n]) * P_g[m][n]
+ *   a_q : [M][K] uint8, a_s : [K/128][M] float32;
+ *   b_q : [N][K] uint8, b_s : [K/128][N] float32 (both as from fp8q_quantize_act
+ *         or fp8q_quantize_act_t);
+ *   c   : [M][N] float32 or bfloat16 (per `out`), row-major (output).
+ *   M >= 0, N % 128 == 0, K % 128 == 0.
+ * FP8Q_ERR_UNSUPPORTED: as fp8q_gemm, with the row-count limit applied to
+ *   both M and N.  Accuracy as fp8q_gemm.
+ */
+fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s,
+                                const uint8_t* b_q, const float* b_s,
+                                int64_t M, int64_t N, int64_t K,
+                                void* c, fp8q_out_dtype out, hipStream_t stream);
+
+/*
  * BF16 GEMM of the same kernel family, without quantization: the reference
  * point for the FP8 path's speed (the-good.kr post 2169793, mixed-precision
  * framework passage: running the GEMMs in FP8 is said to double their speed

@@ -30,7 +30,8 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
-def assert_gemm_close(c_gpu, qa, sa, qw, sw, out="f32", what="", model_rows=16, seed=0):
+def assert_gemm_close(c_gpu, qa, sa, qw, sw, out="f32", what="", model_rows=16, seed=0,
+                      rowscaled=False):
     """Two-tier GEMM parity check; returns a dict of statistics.
 
     c_gpu: numpy [M][N] (float32, or BF16 widened to float64) for the operands
@@ -46,10 +47,17 @@ def assert_gemm_close(c_gpu, qa, sa, qw, sw, out="f32", what="", model_rows=16, 
        that break it must be explained by the hardware's truncation, i.e. lie
        within the tier-1 bound of the model.  The fraction within the strict
        bound is returned.
+
+    rowscaled: the second operand carries 1x128 row-group scales sw [K/128][N]
+    (the weight-gradient GEMM) instead of 128x128 block scales.
     """
     from oracle import mfma_model
-    ref = ogemm.gemm(qa, sa, qw, sw)
-    absb = ogemm.abs_bound(qa, sa, qw, sw)
+    if rowscaled:
+        ref = ogemm.gemm_rowscaled(qa, sa, qw, sw)
+        absb = ogemm.abs_bound_rowscaled(qa, sa, qw, sw)
+    else:
+        ref = ogemm.gemm(qa, sa, qw, sw)
+        absb = ogemm.abs_bound(qa, sa, qw, sw)
     tol = 1e-5 * absb
     half = ogemm.bf16_half_ulp(ref) if out == "bf16" else 0.0
     err = np.abs(c_gpu.astype(np.float64) - ref)
@@ -59,7 +67,8 @@ def assert_gemm_close(c_gpu, qa, sa, qw, sw, out="f32", what="", model_rows=16, 
     rng = np.random.default_rng(seed)
     extra = rng.choice(M, size=min(model_rows, M), replace=False)
     rows = np.unique(np.concatenate([bad_rows, extra])).astype(np.int64)
-    cm = mfma_model.gemm(qa[rows], sa[:, rows], qw, sw)
+    model = mfma_model.gemm_rowscaled if rowscaled else mfma_model.gemm
+    cm = model(qa[rows], sa[:, rows], qw, sw)
     fb = mfma_model.fp32_rounding_bound(qa[rows], sa[:, rows], qw, sw, absb[rows])
     if out == "bf16":
         fb = fb + ogemm.bf16_half_ulp(cm) * (1 + 2.0 ** -7)

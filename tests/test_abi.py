@@ -32,6 +32,9 @@ def lib():
     L.fp8q_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_grouped_gemm.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
     L.fp8q_gemm_bf16.argtypes = [p, p, i64, i64, i64, p, i32, p]
+    L.fp8q_quantize_act_t.argtypes = [p, i64, i64, p, p, i32, p]
+    L.fp8q_quantize_weight_t.argtypes = [p, i64, i64, p, p, i32, p]
+    L.fp8q_gemm_rowscaled.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_status_string.restype = ctypes.c_char_p
     L.fp8q_status_string.argtypes = [ctypes.c_int]
     return L
@@ -47,7 +50,8 @@ def _no_device():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm",
-                          "fp8q_grouped_gemm", "fp8q_gemm_bf16", "fp8q_status_string",
+                          "fp8q_grouped_gemm", "fp8q_gemm_bf16", "fp8q_quantize_act_t",
+                          "fp8q_quantize_weight_t", "fp8q_gemm_rowscaled", "fp8q_status_string",
                           "fp8q_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -141,6 +145,36 @@ def test_gemm_bf16_validation(lib):
     assert f(A, A, 4, 128, (1 << 21) + 128, A, 0, None) == E_UNSUP    # 2K-byte rows
 
 
+def test_transposed_quantizer_validation(lib):
+    for f in (lib.fp8q_quantize_act_t, lib.fp8q_quantize_weight_t):
+        assert f(None, 128, 128, A, A, 0, None) == E_NULL
+        assert f(A, 128, 128, None, A, 0, None) == E_NULL
+        assert f(A, 128, 128, A, None, 0, None) == E_NULL
+        assert f(None, 0, 128, None, None, 0, None) == OK
+        assert f(A, 100, 128, A, A, 0, None) == E_SHAPE   # M (or N) must be a multiple of 128
+        assert f(A, 128, 64, A, A, 0, None) == E_SHAPE
+        assert f(A, -128, 128, A, A, 0, None) == E_SHAPE
+        assert f(A + 8, 128, 128, A, A, 0, None) == E_ALIGN
+        assert f(A, 128, 128, A + 4, A, 0, None) == E_ALIGN
+        assert f(A, 128, 128, A, A + 2, 0, None) == E_ALIGN
+        assert f(A, 128, 128, A, A, 2, None) == E_ENUM
+
+
+def test_gemm_rowscaled_validation(lib):
+    f = lib.fp8q_gemm_rowscaled
+    assert f(A, A, A, A, 4, 128, 128, None, 0, None) == E_NULL
+    assert f(A, A, None, A, 4, 128, 128, A, 0, None) == E_NULL
+    assert f(A, A, A, None, 4, 128, 128, A, 0, None) == E_NULL
+    assert f(A, A, A, A, 4, 100, 128, A, 0, None) == E_SHAPE
+    assert f(A, A, A, A, 4, 128, 64, A, 0, None) == E_SHAPE
+    assert f(A, A, A + 1, A, 4, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A, A, A + 2, 4, 128, 128, A, 0, None) == E_ALIGN
+    assert f(A, A, A, A, 4, 128, 128, A, 3, None) == E_ENUM
+    assert f(None, None, None, None, 0, 128, 128, None, 0, None) == OK
+    assert f(A, A, A, A, 4, 128, 0, A, 0, None) == E_UNSUP
+    assert f(A, A, A, A, 4, 1 << 29, 128, A, 0, None) == E_UNSUP    # b_s offsets >= 2^31
+
+
 def test_valid_arguments_without_gpu_report_device_error(lib):
     if not _no_device():
         pytest.skip("a GPU is visible: fake pointers must not be launched")
@@ -149,3 +183,6 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert lib.fp8q_gemm(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
     assert lib.fp8q_grouped_gemm(A, A, 8, A, 2, A, A, 128, 128, A, 0, None) == E_DEVICE
     assert lib.fp8q_gemm_bf16(A, A, 4, 128, 128, A, 0, None) == E_DEVICE
+    assert lib.fp8q_quantize_act_t(A, 128, 128, A, A, 0, None) == E_DEVICE
+    assert lib.fp8q_quantize_weight_t(A, 128, 128, A, A, 0, None) == E_DEVICE
+    assert lib.fp8q_gemm_rowscaled(A, A, A, A, 4, 128, 128, A, 0, None) == E_DEVICE
