@@ -10,6 +10,11 @@ One step = one pass of the whole path over one batch of synthetic input:
   decode:          activation quantization of ~4352 rows + grouped GEMM over 32
                    experts (M_e uniform in [16, 256]), BF16 output.
   largek:          activation + weight quantization of 8192 x 65536 each + GEMM.
+  backward:        the backward GEMMs of the dense layer (4096 tokens, N 4096,
+                   K 7168) in FP8: Dgrad = 1x128 quantization of dY, transposed
+                   weight quantization, block-scaled GEMM dX = dY W; Wgrad =
+                   transposed (128-token) quantization of dY and X, GEMM with
+                   row-group scales on both operands dW = dY^T X.  FP32 outputs.
   bf16:            the comparison the pages' speed claim calls for: the BF16 GEMM
                    of the same kernel family on the dense shape (BF16 A and W,
                    FP32 out); the FP8 GEMM on the same inputs, quantized once,
@@ -50,7 +55,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "moe", "decode", "largek", "bf16"])
+    p.add_argument("--workload", default="dense", choices=["dense", "moe", "decode", "largek", "bf16", "backward"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -167,6 +172,74 @@ def setup_bf16(fq, torch, sets):
     return step, launch, kernels, flops, cfg
 
 
+def setup_backward(fq, torch, sets):
+    import workloads
+    c = workloads.WORKLOADS["dense"]
+    M, N, K = c["M"], c["N"], c["K"]
+    dev = "cuda:0"
+    X_bits, W_bits = workloads.dense_inputs("dense")
+    dY_bits = workloads.bf16_bits(
+        (np.random.default_rng(c["seed"] + 7).standard_normal((M, N)) * 1e-2).astype(np.float32))
+    to = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+    X0, W0, dY0 = to(X_bits), to(W_bits), to(dY_bits)
+    del X_bits, W_bits, dY_bits
+    f32, u8 = torch.float32, torch.uint8
+    bufs = []
+    for i in range(sets):
+        X = X0 if i == 0 else X0.clone()
+        W = W0 if i == 0 else W0.clone()
+        dY = dY0 if i == 0 else dY0.clone()
+        b = dict(X=X, W=W, dY=dY,
+                 qd=torch.empty((M, N), dtype=u8, device=dev),
+                 sd=torch.empty((N // 128, M), dtype=f32, device=dev),
+                 qwt=torch.empty((K, N), dtype=u8, device=dev),
+                 swt=torch.empty((K // 128, N // 128), dtype=f32, device=dev),
+                 dX=torch.empty((M, K), dtype=f32, device=dev),
+                 qdt=torch.empty((N, M), dtype=u8, device=dev),
+                 sdt=torch.empty((M // 128, N), dtype=f32, device=dev),
+                 qxt=torch.empty((K, M), dtype=u8, device=dev),
+                 sxt=torch.empty((M // 128, K), dtype=f32, device=dev),
+                 dW=torch.empty((N, K), dtype=f32, device=dev))
+        bufs.append(b)
+
+    def launch(name, i):
+        b = bufs[i % sets]
+        if name == "fp8q_quantize_act":
+            fq.fp8q_quantize_act(b["dY"], b["qd"], b["sd"])
+        elif name == "fp8q_quantize_weight_t":
+            fq.fp8q_quantize_weight_t(b["W"], b["qwt"], b["swt"])
+        elif name == "fp8q_gemm":
+            fq.fp8q_gemm(b["qd"], b["sd"], b["qwt"], b["swt"], b["dX"])
+        elif name == "fp8q_quantize_act_t:dY":
+            fq.fp8q_quantize_act_t(b["dY"], b["qdt"], b["sdt"])
+        elif name == "fp8q_quantize_act_t:X":
+            fq.fp8q_quantize_act_t(b["X"], b["qxt"], b["sxt"])
+        else:
+            fq.fp8q_gemm_rowscaled(b["qdt"], b["sdt"], b["qxt"], b["sxt"], b["dW"])
+
+    order = ["fp8q_quantize_act", "fp8q_quantize_weight_t", "fp8q_gemm",
+             "fp8q_quantize_act_t:dY", "fp8q_quantize_act_t:X", "fp8q_gemm_rowscaled"]
+
+    def step(i):
+        for name in order:
+            launch(name, i)
+
+    g = 2.0 * M * N * K
+    kernels = [
+        ("fp8q_quantize_act", "hbm", M * N * ACT_BYTES_PER_ELEM, "B"),
+        ("fp8q_quantize_weight_t", "hbm", N * K * WEIGHT_BYTES_PER_ELEM, "B"),
+        ("fp8q_gemm", "mfma", g, "flop"),
+        ("fp8q_quantize_act_t:dY", "hbm", M * N * ACT_BYTES_PER_ELEM, "B"),
+        ("fp8q_quantize_act_t:X", "hbm", M * K * ACT_BYTES_PER_ELEM, "B"),
+        ("fp8q_gemm_rowscaled", "mfma", g, "flop"),
+    ]
+    cfg = {"workload": f"backward: tokens {M}, N {N}, K {K}; Dgrad dX = dY W (1x128 quant of dY, "
+                       f"transposed 128x128 quant of W, block-scaled GEMM) + Wgrad dW = dY^T X "
+                       f"(128-token quant of dY and X, row-scaled GEMM), fp32 out",
+           "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
+    return step, launch, kernels, 2 * g, cfg
+
+
 def setup_grouped(fq, torch, name, sets):
     import workloads
     c = workloads.WORKLOADS[name]
@@ -277,6 +350,23 @@ def cpu_baseline(name):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    if name == "backward":
+        c = workloads.WORKLOADS["dense"]
+        M, N, K = c["M"], c["N"], c["K"]
+        rows = 256
+        X, _ = workloads.dense_inputs("dense", rows_w=np.arange(128))
+        dY = workloads.bf16_bits(
+            (np.random.default_rng(c["seed"] + 7).standard_normal((M, N)) * 1e-2).astype(np.float32))
+        t0 = time.perf_counter()
+        qdt, sdt = oquant.quantize_act_t(dY)
+        qxt, sxt = oquant.quantize_act_t(X)
+        ogemm.gemm_rowscaled(qdt[:rows], sdt[:, :rows], qxt, sxt)
+        dt = time.perf_counter() - t0
+        flops = 2.0 * rows * K * M
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                "sample": f"Wgrad rows 0..{rows - 1} of dW: oracle quantize_act_t of dY ({M}x{N}) "
+                          f"and X ({M}x{K}) + exact row-scaled GEMM {rows}x{K}x{M}; {dt:.1f} s wall; "
+                          f"value = 2*{rows}*{K}*{M} / wall"}
     if name == "bf16":
         c = workloads.WORKLOADS["dense"]
         M, N, K = c["M"], c["N"], c["K"]
@@ -329,11 +419,13 @@ def main():
     import fine_grained_block_fp8q_amd as fq
 
     sets = args.sets or (4 if args.workload in ("dense", "bf16") else
-                         2 if args.workload == "decode" else 1)
+                         2 if args.workload in ("decode", "backward") else 1)
     if args.workload in ("dense", "largek"):
         step, launch, kernels, flops, cfg = setup_dense(fq, torch, args.workload, sets)
     elif args.workload == "bf16":
         step, launch, kernels, flops, cfg = setup_bf16(fq, torch, sets)
+    elif args.workload == "backward":
+        step, launch, kernels, flops, cfg = setup_backward(fq, torch, sets)
     else:
         step, launch, kernels, flops, cfg = setup_grouped(fq, torch, args.workload, sets)
     torch.cuda.synchronize()
@@ -398,6 +490,11 @@ def main():
             "same_kernel_family": dom["avg_us"] / kout["fp8q_gemm"]["avg_us"],
             "hipblaslt_bf16_out": (kout["torch_matmul_bf16_hipblaslt"]["avg_us"]
                                    / kout["fp8q_gemm"]["avg_us"])}
+    elif args.workload == "backward":
+        dom = kout["fp8q_gemm_rowscaled"]
+        roof = {"kernel": "fp8q_gemm_rowscaled", "bound": "mfma", "achieved": dom["TFLOP_s"],
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": dom["TFLOP_s"] / PEAK_FP8_TFLOPS,
+                "traffic": recorded_traffic("fp8q_gemm_rowscaled", cfg)}
     elif args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm"]
         traffic = recorded_traffic("fp8q_gemm", cfg)

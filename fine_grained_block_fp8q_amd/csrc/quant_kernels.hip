@@ -211,8 +211,9 @@ __device__ __forceinline__ float bf16_at(const uint4& v, int j) {
   return (j & 1) ? bf16_hi(w) : bf16_lo(w);
 }
 
-__device__ __forceinline__ void store_code_word(uint8_t* dst, uint32_t w) {
-  __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(dst));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_piece(uint8_t* dst, const uint4 o) {
+  __builtin_nontemporal_store(v4u{o.x, o.y, o.z, o.w}, reinterpret_cast<v4u*>(dst));
 }
 
 // Activations, transposed: x[M][K] -> q_t[K][M], s_t[M/128][K].  A workgroup
@@ -221,14 +222,19 @@ __device__ __forceinline__ void store_code_word(uint8_t* dst, uint32_t w) {
 // row's 128 contiguous bytes.  A column's max-abs is reduced over the lane's
 // 4 rows, across the 8 lanes of the wave that share cp (shuffles), then
 // across the 4 waves through LDS.  The lane packs the codes of its 4
-// consecutive rows of each column into one word of that column's output row:
-// the 8 lanes of a wave with equal cp write 32 contiguous bytes of it, and the
-// 4 waves the whole 128.
+// consecutive rows of each column into one word of the tile's transposed copy
+// in LDS (64 output rows of 128 bytes); the workgroup then stores that copy
+// with one 16-byte store per lane and piece, 8 lanes per 128-byte output row.
+// (Storing the words straight to HBM, 32-byte runs per row and wave, ran at
+// half the rate.)
+constexpr int kTRow = 144;  // bytes per row of a transposed code tile in LDS (16-byte aligned)
+
 template <int MODE>
 __global__ __launch_bounds__(256) void quantize_act_t_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, uint8_t* __restrict__ qt,
     float* __restrict__ st, int64_t n_kblk) {
   __shared__ float red[4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * kTRow];
   const int64_t bid = blockIdx.x;
   const int64_t kb = bid % n_kblk;  // 64-column block (fastest: neighbours share rows)
   const int64_t mb = bid / n_kblk;  // group of 128 rows
@@ -261,7 +267,16 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(
     if (rq == 0) st[mb * K + k0 + j] = r.s;
     const uint32_t w = pack_e4m3x4(apply<MODE>(bf16_at(v[0], j), r), apply<MODE>(bf16_at(v[1], j), r),
                                    apply<MODE>(bf16_at(v[2], j), r), apply<MODE>(bf16_at(v[3], j), r));
-    store_code_word(qt + (k0 + j) * M + m0, w);
+    *reinterpret_cast<uint32_t*>(tile + c * kTRow + 4 * rq) = w;
+  }
+  __syncthreads();
+  // 64 rows x 128 bytes = 512 pieces of 16 bytes, 2 per lane.
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int p = t + 256 * u;
+    const int row = p >> 3, piece = p & 7;
+    const uint4 o = *reinterpret_cast<const uint4*>(tile + row * kTRow + 16 * piece);
+    store_piece(qt + (kb * 64 + row) * M + mb * kGroup + 16 * piece, o);
   }
 }
 
@@ -269,13 +284,15 @@ __global__ __launch_bounds__(256) void quantize_act_t_kernel(
 // workgroup per 128x128 block: lane (rq = t/16, cp = t%16) loads rows
 // 8rq .. 8rq+7 at columns 8cp .. 8cp+7 (16 lanes read a row's 256 bytes).
 // The block max is reduced as in quantize_weight_kernel (each DPP row is one
-// rq); each lane then writes 8 bytes, its 8 consecutive rows, of each of its 8
-// columns' output rows.
+// rq); each lane then writes the codes of its 8 consecutive rows of each of
+// its 8 columns (8 bytes) into the block's transposed copy in LDS, which the
+// workgroup stores with 16-byte pieces, 8 lanes per 128-byte output row.
 template <int MODE>
 __global__ __launch_bounds__(256) void quantize_weight_t_kernel(
     const uint16_t* __restrict__ w, int64_t N, int64_t K, uint8_t* __restrict__ qt,
     float* __restrict__ st, int64_t KB) {
   __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kTRow];
   const int64_t bid = blockIdx.x;
   const int64_t nb = bid / KB;
   const int64_t kb = bid % KB;
@@ -307,9 +324,18 @@ __global__ __launch_bounds__(256) void quantize_weight_t_kernel(
                       apply<MODE>(bf16_at(v[2], j), r), apply<MODE>(bf16_at(v[3], j), r));
     o.y = pack_e4m3x4(apply<MODE>(bf16_at(v[4], j), r), apply<MODE>(bf16_at(v[5], j), r),
                       apply<MODE>(bf16_at(v[6], j), r), apply<MODE>(bf16_at(v[7], j), r));
-    store_codes(qt + (k0 + j) * N + n0, o);
+    *reinterpret_cast<uint2*>(tile + (8 * cp + j) * kTRow + 8 * rq) = o;
   }
   if (t == 0) st[kb * (N / kGroup) + nb] = r.s;
+  __syncthreads();
+  // 128 rows x 128 bytes = 1024 pieces of 16 bytes, 4 per lane.
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int p = t + 256 * u;
+    const int row = p >> 3, piece = p & 7;
+    const uint4 o = *reinterpret_cast<const uint4*>(tile + row * kTRow + 16 * piece);
+    store_piece(qt + (kb * kGroup + row) * N + nb * kGroup + 16 * piece, o);
+  }
 }
 
 hipError_t launch_quantize_act_t(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
