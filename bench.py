@@ -309,13 +309,17 @@ GEMM_SOURCES = ("gemm_kernels.hip", "gemm_common.hpp", "fp8q_device.hpp")
 
 
 def kernel_source_digest():
-    """sha256 over the GEMM kernels' sources (in GEMM_SOURCES order): traffic
-    figures recorded under profiles/ are reported only while they are
-    unchanged."""
+    """sha256 over the code of the GEMM kernels' sources (in GEMM_SOURCES
+    order, with comments and whitespace removed): traffic figures recorded
+    under profiles/ are reported only while that code is unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in GEMM_SOURCES:
-        h.update(open(os.path.join(ROOT, "fine_grained_block_fp8q_amd", "csrc", name), "rb").read())
+        text = open(os.path.join(ROOT, "fine_grained_block_fp8q_amd", "csrc", name)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()
 
 

@@ -31,6 +31,13 @@
 // bank-conflict free.  The dense kernel's two-stage ring is backed by an L2
 // prefetch several chunks ahead, split between the tiles that share a band
 // of A or W rows in one XCD's L2.
+//
+// The same tile serves three more configurations (GemmCfg flags): the
+// weight-gradient GEMM, whose weight-side operand carries 1x128 row-group
+// scales like the activations (W_ROWSCALE: the multiplier differs per output
+// element); BF16 operands without scales (OP_BF16: the reference of the FP8
+// path, accumulating in the matrix core); and the grouped MoE kernel's
+// row-count buckets (persistent workgroups, see grouped_gemm_kernel).
 
 #include "gemm_common.hpp"
 
