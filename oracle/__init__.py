@@ -18,7 +18,7 @@ numbers, so the passage is named by topic):
 * [whybe-57820] why-be.co.kr as_center post 57820 -- the promotion passage
   (partial results copied out of the matrix unit every N_C interval, multiplied
   by the scaling factors, added into FP32 registers) and the hardware
-  suggestion "Higher FP8 GEMM Accumulation Precision in Tensor Cores".
+  suggestion of higher-precision FP8 accumulation inside the matrix units.
 * [pkd-78017] pkd.ac.th webboard post 78017 -- the increased-precision
   accumulation passage (128 elements, i.e. four WGMMAs, is the smallest
   promotion interval that helps).
@@ -28,8 +28,13 @@ numbers, so the passage is named by topic):
 
 Modules:
   e4m3        OCP E4M3 (E4M3FN) decode table and round-to-nearest-even encoder
-  quant       1x128 activation / 128x128 weight quantizers (FP32 and pow2 scales)
-  gemm        block-scaled GEMM with per-128-K promotion, exact in float64
+  quant       1x128 activation / 128x128 weight quantizers (FP32 and pow2
+              scales), their transposed forms for the backward GEMMs, and
+              per-tensor scaling (accuracy study)
+  gemm        block-scaled GEMM with per-128-K promotion, exact in float64; the
+              variant with row-group scales on both operands (weight gradient);
+              the BF16 reference product
+  mfma_model  model of the gfx950 FP8 matrix core's dot product (parity tier 1)
   narrow_acc  emulator of a narrow fixed-point accumulator (accuracy study)
 """
 
