@@ -88,3 +88,24 @@ def test_model_gemm_close_to_exact_on_random_data():
     bound = gemm.abs_bound(qa, sa, qw, sw)
     rel = np.abs(Cm - Ce) / bound
     assert rel.max() < 2e-4 and rel.max() > 0  # narrow, but not exact
+
+
+def test_rowscaled_model_reduces_to_block_scaled():
+    """The weight-gradient variant of the model equals the block-scaled model
+    when the second operand's row scales are constant over 128-row blocks
+    (sb[g][n] = sw[n // 128][g]), and is linear in one row's scale."""
+    import workloads
+    from oracle import quant
+    rng = np.random.default_rng(31)
+    A = workloads.bf16_bits(rng.standard_normal((3, 256)).astype(np.float32))
+    W = workloads.bf16_bits((rng.standard_normal((256, 256)) * 0.02).astype(np.float32))
+    qa, sa = quant.quantize_act(A)
+    qw, sw = quant.quantize_weight(W)
+    sb = np.repeat(sw, 128, axis=0).T.copy()  # [K/128][N]
+    assert np.array_equal(mfma_model.gemm_rowscaled(qa, sa, qw, sb), mfma_model.gemm(qa, sa, qw, sw))
+    sb2 = sb.copy()
+    sb2[:, 5] *= np.float32(4.0)
+    c1 = mfma_model.gemm_rowscaled(qa, sa, qw, sb)
+    c2 = mfma_model.gemm_rowscaled(qa, sa, qw, sb2)
+    assert np.array_equal(c2[:, 5], 4.0 * c1[:, 5])
+    assert np.array_equal(np.delete(c2, 5, axis=1), np.delete(c1, 5, axis=1))
