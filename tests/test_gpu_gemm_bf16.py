@@ -88,3 +88,28 @@ def test_bf16_gemm_determinism():
     c1 = _run(A, W)
     c2 = _run(A, W)
     assert np.array_equal(c1, c2)
+
+
+def test_fp8_path_error_against_bf16_on_dense_workload():
+    """Accuracy of the FP8 path on the dense workload (1% x30 outlier channels),
+    against the exact product of its BF16 inputs on 32 sampled rows: the FP8
+    GEMM carries the E4M3 quantization error (a few percent, as the oracle's
+    outlier study predicts); the BF16 GEMM of the same family only FP32
+    rounding.  The pages give no magnitude for this, so only the order is
+    asserted."""
+    cfg = workloads.WORKLOADS["dense"]
+    A, W = workloads.dense_inputs("dense")
+    f = fq()
+    a, w = to_dev_bf16(A), to_dev_bf16(W)
+    aq, as_ = f.quantize_act(a)
+    wq, ws = f.quantize_weight(w)
+    c8 = f.gemm(aq, as_, wq, ws)
+    c16 = torch.empty_like(c8)
+    f.fp8q_gemm_bf16(a, w, c16)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(cfg["M"], 32, replace=False))
+    ref = ogemm.gemm_bf16(A[rows], W)
+    e8 = np.linalg.norm(c8.cpu().numpy()[rows] - ref) / np.linalg.norm(ref)
+    e16 = np.linalg.norm(c16.cpu().numpy()[rows] - ref) / np.linalg.norm(ref)
+    print(f"relative Frobenius error vs the exact BF16 product: FP8 path {e8:.3e}, BF16 GEMM {e16:.3e}")
+    assert e16 < 1e-6 and 1e-3 < e8 < 0.06
