@@ -15,6 +15,10 @@ One step = one pass of the whole path over one batch of synthetic input:
                    weight quantization, block-scaled GEMM dX = dY W; Wgrad =
                    transposed (128-token) quantization of dY and X, GEMM with
                    row-group scales on both operands dW = dY^T X.  FP32 outputs.
+  dense_fused,     the activation quantization fused into the GEMM (the FP8 cast
+  decode_fused:    during the transfer the pages ask for): the same steps with
+                   fp8q_gemm_fused / fp8q_grouped_gemm_fused in place of
+                   fp8q_quantize_act + the GEMM; both are timed per kernel.
   bf16:            the comparison the pages' speed claim calls for: the BF16 GEMM
                    of the same kernel family on the dense shape (BF16 A and W,
                    FP32 out); the FP8 GEMM on the same inputs, quantized once,
@@ -55,7 +59,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="dense", choices=["dense", "moe", "decode", "largek", "bf16", "backward"])
+    p.add_argument("--workload", default="dense",
+                   choices=["dense", "moe", "decode", "largek", "bf16", "backward", "dense_fused",
+                            "decode_fused"])
     p.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -81,7 +87,7 @@ def gemm_bytes(M, N, K, out_bytes):
 
 
 # --------------------------------------------------------------------- setup
-def setup_dense(fq, torch, name, sets):
+def setup_dense(fq, torch, name, sets, fused=False):
     import workloads
     c = workloads.WORKLOADS[name]
     M, N, K = c["M"], c["N"], c["K"]
@@ -107,10 +113,13 @@ def setup_dense(fq, torch, name, sets):
             fq.fp8q_quantize_act(A, aq, as_)
         elif name == "fp8q_quantize_weight":
             fq.fp8q_quantize_weight(W, wq, ws)
+        elif name == "fp8q_gemm_fused":
+            fq.fp8q_gemm_fused(A, wq, ws, C)
         else:
             fq.fp8q_gemm(aq, as_, wq, ws, C)
 
-    order = ["fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm"]
+    order = (["fp8q_quantize_weight", "fp8q_gemm_fused"] if fused else
+             ["fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm"])
 
     def step(i):
         for name in order:
@@ -121,8 +130,12 @@ def setup_dense(fq, torch, name, sets):
         ("fp8q_quantize_weight", "hbm", N * K * WEIGHT_BYTES_PER_ELEM, "B"),
         ("fp8q_gemm", "mfma", 2.0 * M * N * K, "flop"),
     ]
+    if fused:
+        kernels.insert(0, ("fp8q_gemm_fused", "mfma", 2.0 * M * N * K, "flop"))
     flops = 2.0 * M * N * K
-    cfg = {"workload": f"{name}: A {M}x{K} bf16 (1x128 act quant), W {N}x{K} bf16 "
+    tag = name + ("_fused" if fused else "")
+    how = "quantized inside the GEMM" if fused else "1x128 act quant"
+    cfg = {"workload": f"{tag}: A {M}x{K} bf16 ({how}), W {N}x{K} bf16 "
                        f"(128x128 block quant), C = A W^T fp32",
            "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
     return step, launch, kernels, flops, cfg
@@ -240,7 +253,7 @@ def setup_backward(fq, torch, sets):
     return step, launch, kernels, 2 * g, cfg
 
 
-def setup_grouped(fq, torch, name, sets):
+def setup_grouped(fq, torch, name, sets, fused=False):
     import workloads
     c = workloads.WORKLOADS[name]
     dev = "cuda:0"
@@ -283,12 +296,17 @@ def setup_grouped(fq, torch, name, sets):
         A, aq, as_, C = bufs[i % sets]
         if name == "fp8q_quantize_act":
             fq.fp8q_quantize_act(A, aq, as_)
+        elif name == "fp8q_grouped_gemm_fused":
+            fq.fp8q_grouped_gemm_fused(A, d_off, wq, ws, C)
         else:
             fq.fp8q_grouped_gemm(aq, as_, d_off, wq, ws, C)
 
     def step(i):
-        launch("fp8q_quantize_act", i)
-        launch("fp8q_grouped_gemm", i)
+        if fused:
+            launch("fp8q_grouped_gemm_fused", i)
+        else:
+            launch("fp8q_quantize_act", i)
+            launch("fp8q_grouped_gemm", i)
 
     ob = 2 if out_dtype == torch.bfloat16 else 4
     flops = 2.0 * Mt * N * K
@@ -297,15 +315,22 @@ def setup_grouped(fq, torch, name, sets):
         ("fp8q_quantize_act", "hbm", Mt * K * ACT_BYTES_PER_ELEM, "B"),
         ("fp8q_grouped_gemm", "hbm", gbytes, "B"),
     ]
-    cfg = {"workload": f"{name}: {G} experts, rows {Mt} (M_e {int(counts.min())}..{int(counts.max())}), "
-                       f"N {N}, K {K}, 1x128 act quant + grouped GEMM, weights pre-quantized 128x128",
+    if fused:
+        # weights and their scales once, the BF16 activations once, the output
+        fbytes = G * N * K * (1 + 4 / 16384) + Mt * K * 2 + Mt * N * ob
+        kernels.insert(0, ("fp8q_grouped_gemm_fused", "hbm", fbytes, "B"))
+    tag = name + ("_fused" if fused else "")
+    how = ("grouped GEMM quantizing its BF16 activations (1x128) inside" if fused else
+           "1x128 act quant + grouped GEMM")
+    cfg = {"workload": f"{tag}: {G} experts, rows {Mt} (M_e {int(counts.min())}..{int(counts.max())}), "
+                       f"N {N}, K {K}, {how}, weights pre-quantized 128x128",
            "experts": G, "rows": Mt, "N": N, "K": K, "out": "bf16" if ob == 2 else "f32",
            "input_sets": sets}
     return step, launch, kernels, flops, cfg
 
 
 # -------------------------------------------------------- recorded traffic
-GEMM_SOURCES = ("gemm_kernels.hip", "gemm_common.hpp", "fp8q_device.hpp")
+GEMM_SOURCES = ("gemm_kernels.hip", "gemm_common.hpp", "fp8q_device.hpp", "quant_rules.hpp")
 
 
 def kernel_source_digest():
@@ -422,16 +447,18 @@ def main():
     import torch
     import fine_grained_block_fp8q_amd as fq
 
-    sets = args.sets or (4 if args.workload in ("dense", "bf16") else
-                         2 if args.workload in ("decode", "backward") else 1)
-    if args.workload in ("dense", "largek"):
-        step, launch, kernels, flops, cfg = setup_dense(fq, torch, args.workload, sets)
+    sets = args.sets or (4 if args.workload in ("dense", "bf16", "dense_fused") else
+                         2 if args.workload in ("decode", "backward", "decode_fused") else 1)
+    base = args.workload.replace("_fused", "")
+    fused = base != args.workload
+    if base in ("dense", "largek"):
+        step, launch, kernels, flops, cfg = setup_dense(fq, torch, base, sets, fused)
     elif args.workload == "bf16":
         step, launch, kernels, flops, cfg = setup_bf16(fq, torch, sets)
     elif args.workload == "backward":
         step, launch, kernels, flops, cfg = setup_backward(fq, torch, sets)
     else:
-        step, launch, kernels, flops, cfg = setup_grouped(fq, torch, args.workload, sets)
+        step, launch, kernels, flops, cfg = setup_grouped(fq, torch, base, sets, fused)
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps, synchronized on both sides.
@@ -499,6 +526,26 @@ def main():
         roof = {"kernel": "fp8q_gemm_rowscaled", "bound": "mfma", "achieved": dom["TFLOP_s"],
                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": dom["TFLOP_s"] / PEAK_FP8_TFLOPS,
                 "traffic": recorded_traffic("fp8q_gemm_rowscaled", cfg)}
+    elif args.workload == "dense_fused":
+        dom = kout["fp8q_gemm_fused"]
+        roof = {"kernel": "fp8q_gemm_fused", "bound": "mfma", "achieved": dom["TFLOP_s"],
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": dom["TFLOP_s"] / PEAK_FP8_TFLOPS,
+                "traffic": recorded_traffic("fp8q_gemm_fused", cfg),
+                "fused_vs_separate_us": {
+                    "fused": dom["avg_us"],
+                    "quantize_act_plus_gemm": (kout["fp8q_quantize_act"]["avg_us"]
+                                               + kout["fp8q_gemm"]["avg_us"])}}
+    elif args.workload == "decode_fused":
+        dom = kout["fp8q_grouped_gemm_fused"]
+        dom["TFLOP_s"] = flops / (dom["avg_us"] * 1e-6) / 1e12
+        dom["frac_fp8_peak"] = dom["TFLOP_s"] / PEAK_FP8_TFLOPS
+        roof = {"kernel": "fp8q_grouped_gemm_fused", "bound": "hbm", "achieved": dom["GB_s"],
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom["GB_s"] / PEAK_HBM_GBS,
+                "traffic": recorded_traffic("fp8q_grouped_gemm_fused", cfg),
+                "fused_vs_separate_us": {
+                    "fused": dom["avg_us"],
+                    "quantize_act_plus_grouped_gemm": (kout["fp8q_quantize_act"]["avg_us"]
+                                                       + kout["fp8q_grouped_gemm"]["avg_us"])}}
     elif args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm"]
         traffic = recorded_traffic("fp8q_gemm", cfg)
@@ -522,7 +569,7 @@ def main():
            "data": "synthetic (seeded; shapes and distributions of the workload table)",
            "config": cfg, "roofline": roof, "kernels": kout}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(args.workload)
+        rec["cpu_baseline"] = cpu_baseline(base)
     print(json.dumps(rec), flush=True)
 
 

@@ -46,6 +46,11 @@ lib.fp8q_quantize_weight_t.restype = _st
 lib.fp8q_gemm_rowscaled.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_gemm_rowscaled.restype = _st
 lib.fp8q_gemm_bf16.restype = _st
+lib.fp8q_gemm_fused.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p]
+lib.fp8q_gemm_fused.restype = _st
+lib.fp8q_grouped_gemm_fused.argtypes = [_p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32, _i32,
+                                        _p]
+lib.fp8q_grouped_gemm_fused.restype = _st
 lib.fp8q_status_string.argtypes = [_st]
 lib.fp8q_status_string.restype = ctypes.c_char_p
 lib.fp8q_abi_version.argtypes = []
@@ -121,6 +126,30 @@ def fp8q_grouped_gemm(a_q, a_s, off, w_q, w_s, c, stream=None):
     _check(lib.fp8q_grouped_gemm(_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
                                  _ptr(w_s), N, K, _ptr(c), out, _stream(stream, a_q.device)),
            "fp8q_grouped_gemm")
+
+
+def fp8q_gemm_fused(x, w_q, w_s, c, mode="f32", stream=None):
+    """c[M][N] = fp8q_gemm(quantize_act(x, mode), w_q, w_s), x: bf16 [M][K]
+    quantized inside the GEMM."""
+    import torch
+    M, K = x.shape
+    N = w_q.shape[0]
+    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    _check(lib.fp8q_gemm_fused(_ptr(x), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
+                               _MODES[mode], _stream(stream, x.device)), "fp8q_gemm_fused")
+
+
+def fp8q_grouped_gemm_fused(x, off, w_q, w_s, c, mode="f32", stream=None):
+    """The grouped GEMM of quantize_act(x, mode), x: bf16 [M_total][K]
+    quantized inside the GEMM; off is a device int32[G+1]."""
+    import torch
+    M_total, K = x.shape
+    G, N, _ = w_q.shape
+    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    _check(lib.fp8q_grouped_gemm_fused(_ptr(x), M_total, _ptr(off), G, _ptr(w_q), _ptr(w_s), N,
+                                       K, _ptr(c), out, _MODES[mode],
+                                       _stream(stream, x.device)),
+           "fp8q_grouped_gemm_fused")
 
 
 def fp8q_gemm_bf16(a, w, c, stream=None):
@@ -207,6 +236,22 @@ def gemm(a_q, a_s, w_q, w_s, out_dtype=None, stream=None):
     out_dtype = out_dtype or torch.float32
     c = torch.empty((a_q.shape[0], w_q.shape[0]), dtype=out_dtype, device=a_q.device)
     fp8q_gemm(a_q, a_s, w_q, w_s, c, stream)
+    return c
+
+
+def gemm_fused(x, w_q, w_s, mode="f32", out_dtype=None, stream=None):
+    import torch
+    out_dtype = out_dtype or torch.float32
+    c = torch.empty((x.shape[0], w_q.shape[0]), dtype=out_dtype, device=x.device)
+    fp8q_gemm_fused(x, w_q, w_s, c, mode, stream)
+    return c
+
+
+def grouped_gemm_fused(x, off, w_q, w_s, mode="f32", out_dtype=None, stream=None):
+    import torch
+    out_dtype = out_dtype or torch.float32
+    c = torch.empty((x.shape[0], w_q.shape[1]), dtype=out_dtype, device=x.device)
+    fp8q_grouped_gemm_fused(x, off, w_q, w_s, c, mode, stream)
     return c
 
 

@@ -33,8 +33,11 @@ COMMON = [
 SOURCES = {
     "quant_kernels.hip": ["-ffp-contract=off"],
     # keep MFMA results in arch VGPRs: the promotion FMAs read them directly
-    # instead of copying each element out of an AGPR first
-    "gemm_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # instead of copying each element out of an AGPR first; let the main
+    # loop's step sequence unroll fully also with the activation cast in it
+    # (left rolled, its register arrays would go to scratch memory)
+    "gemm_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                         "-mllvm", "-pragma-unroll-threshold=60000"],
     "fp8q_api.hip": [],
 }
 

@@ -31,6 +31,12 @@ hipError_t launch_quantize_weight_t(const void* w, int64_t N, int64_t K, uint8_t
 hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
                                  const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
                                  int out_bf16, hipStream_t stream);
+hipError_t launch_gemm_cast(const void* x, const uint8_t* w_q, const float* w_s, int64_t M,
+                            int64_t N, int64_t K, void* c, int out_bf16, int mode,
+                            hipStream_t stream);
+hipError_t launch_grouped_gemm_cast(const void* x, int64_t M_total, const int32_t* off, int G,
+                                    const uint8_t* w_q, const float* w_s, int64_t N, int64_t K,
+                                    void* c, int out_bf16, int mode, hipStream_t stream);
 }  // namespace fp8q
 
 namespace {
@@ -235,6 +241,52 @@ fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, i
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_gemm_bf16(a, w, M, N, K, c, out == FP8Q_OUT_BF16, stream));
+}
+
+// The fused GEMMs read 2K-byte BF16 activation rows through 32-bit buffer
+// offsets (row-in-tile * 2K): K up to 2^21, as for the BF16 GEMM.
+fp8q_status fp8q_gemm_fused(const void* x_bf16, const uint8_t* w_q, const float* w_s,
+                            int64_t M, int64_t N, int64_t K, void* c, fp8q_out_dtype out,
+                            fp8q_scale_mode mode, hipStream_t stream) {
+  const bool empty_out = (M == 0 || N == 0);
+  if (!empty_out && !c) return FP8Q_ERR_NULL;
+  if (!empty_out && K != 0 && (!x_bf16 || !w_q || !w_s)) return FP8Q_ERR_NULL;
+  if (M < 0 || N < 0 || K < 0 || N % 128 != 0 || K % 128 != 0) return FP8Q_ERR_SHAPE;
+  if (!aligned(x_bf16, 16) || !aligned(w_q, 16) || !aligned(c, 16) || !aligned(w_s, 4))
+    return FP8Q_ERR_ALIGN;
+  if (!valid_out(out) || !valid_mode(mode)) return FP8Q_ERR_ENUM;
+  if (empty_out) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_UNSUPPORTED;
+  if (K > (int64_t(1) << 21)) return FP8Q_ERR_UNSUPPORTED;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_gemm_cast(x_bf16, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16,
+                                         (int)mode, stream));
+}
+
+fp8q_status fp8q_grouped_gemm_fused(const void* x_bf16, int64_t M_total, const int32_t* off,
+                                    int32_t G, const uint8_t* w_q, const float* w_s, int64_t N,
+                                    int64_t K, void* c, fp8q_out_dtype out, fp8q_scale_mode mode,
+                                    hipStream_t stream) {
+  const bool empty_out = (M_total == 0 || N == 0);
+  if (!off) return FP8Q_ERR_NULL;
+  if (!empty_out && !c) return FP8Q_ERR_NULL;
+  if (!empty_out && K != 0 && (!x_bf16 || !w_q || !w_s)) return FP8Q_ERR_NULL;
+  if (M_total < 0 || N < 0 || K < 0 || G < 1 || N % 128 != 0 || K % 128 != 0)
+    return FP8Q_ERR_SHAPE;
+  if (G > 1024) return FP8Q_ERR_UNSUPPORTED;
+  if (M_total > 0x7FFFFFFF) return FP8Q_ERR_SHAPE;  // offsets are int32
+  if (!aligned(x_bf16, 16) || !aligned(w_q, 16) || !aligned(c, 16) || !aligned(w_s, 4) ||
+      !aligned(off, 4))
+    return FP8Q_ERR_ALIGN;
+  if (!valid_out(out) || !valid_mode(mode)) return FP8Q_ERR_ENUM;
+  if (empty_out) return FP8Q_OK;
+  if (K == 0) return FP8Q_ERR_UNSUPPORTED;
+  if (K > (int64_t(1) << 21)) return FP8Q_ERR_UNSUPPORTED;
+  const fp8q_status d = check_device();
+  if (d != FP8Q_OK) return d;
+  return launched(fp8q::launch_grouped_gemm_cast(x_bf16, M_total, off, G, w_q, w_s, N, K, c,
+                                                 out == FP8Q_OUT_BF16, (int)mode, stream));
 }
 
 }  // extern "C"

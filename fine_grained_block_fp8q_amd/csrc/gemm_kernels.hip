@@ -40,6 +40,7 @@
 // row-count buckets (persistent workgroups, see grouped_gemm_kernel).
 
 #include "gemm_common.hpp"
+#include "quant_rules.hpp"
 
 namespace fp8q {
 
@@ -51,11 +52,16 @@ namespace fp8q {
 // ([K/128][N], like the activations) instead of 128x128 block scales: the
 // weight-gradient GEMM, whose operands dY^T and X^T are both grouped along
 // the tokens.  The multiplier then differs per output element.
+// A_CAST_: 0 = the activation codes and row scales are loaded as they are;
+// 1 (FP32 scales) or 2 (power-of-two scales) = the activations arrive as BF16
+// and are quantized on their way into LDS (ACaster).
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int ROWS_ = BM_,
-          int PF_ = 0, int OP_BF16_ = 0, int W_ROWSCALE_ = 0>
+          int PF_ = 0, int OP_BF16_ = 0, int W_ROWSCALE_ = 0, int A_CAST_ = 0>
 struct GemmCfg {
   static constexpr bool OP_BF16 = OP_BF16_ != 0;
   static constexpr bool W_ROWSCALE = W_ROWSCALE_ != 0;
+  static constexpr bool A_CAST = A_CAST_ != 0;
+  static constexpr int CAST_MODE = A_CAST ? A_CAST_ - 1 : 0;
   static constexpr int SUB = OP_BF16 ? 2 : 1;       // MFMAs per 16x16 block per chunk
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -78,11 +84,13 @@ struct GemmCfg {
   static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
   static constexpr int PF_BYTES = PF_LOADS > 0 ? NWAVES * 256 : 0;  // their LDS landing slots
   static constexpr int LDS_BYTES = STAGE * STAGES + PF_BYTES;
-  static constexpr int A_BLK = A_BYTES / 1024;      // 1 KiB load instructions for A
+  static constexpr int A_BLK = A_CAST ? 0 : A_BYTES / 1024;  // 1 KiB load instructions for A
   static constexpr int OP_BLK = A_BLK + B_BYTES / 1024;
   static constexpr int PER_WAVE = (OP_BLK + NWAVES - 1) / NWAVES;  // operand loads per wave
   static constexpr int PAD = PER_WAVE * NWAVES - OP_BLK;  // repeated A loads that even them out
-  static constexpr int LOADS = PER_WAVE + (OP_BF16 ? 0 : 1) + (W_ROWSCALE ? 1 : 0);  // + scales
+  static constexpr int LOADS =
+      PER_WAVE + (OP_BF16 || A_CAST ? 0 : 1) + (W_ROWSCALE ? 1 : 0);  // + scales
+  static constexpr int CAST_ROUNDS = A_CAST ? (ROWS + 63) / 64 : 0;  // 64 rows per round
   static_assert(WM % 16 == 0 && WM <= 64, "a wave's rows fit one 256-byte scale slot");
   static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
   // Staged rows: whole 1 KiB loads.  When they stop inside a wave (160 rows
@@ -97,6 +105,9 @@ struct GemmCfg {
   static_assert(LOADS * (STAGES - 1) + PF_LOADS * (STAGES - 1) < 64, "vmcnt range");
   static_assert(!W_ROWSCALE || (!OP_BF16 && NWAVES == 8 && BN == 256 && WN == 128),
                 "row-scaled weights: 8 waves, each loading 64 of the 256 row scales");
+  static_assert(!A_CAST || (!OP_BF16 && !W_ROWSCALE && PF_LOADS == 0 && THREADS == 512 &&
+                            A_CAST_ <= 2 && CAST_ROUNDS <= 4),
+                "activation cast: 512 lanes, 8 per row, FP8 block-scaled weights");
 };
 
 // Dense configuration: 256 x 256 tiles, 8 waves (two per SIMD, so one wave's
@@ -108,6 +119,10 @@ using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 using DenseBf16Cfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 1>;
 // The weight-gradient GEMM: the dense tile with row-scaled weights.
 using RowScaledCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 0, 1>;
+// BF16 activations quantized inside the GEMM (scale mode MODE): the dense
+// tile without the L2 prefetch, whose A lines would be BF16 rows.
+template <int MODE>
+using DenseCastCfg = GemmCfg<256, 256, 4, 2, 2, 256, 0, 0, 0, 1 + MODE>;
 // Grouped configurations: 256-row tiles cover an expert's tokens (decode
 // batches hold at most 256) so each expert's weights stream once, and 256
 // weight rows per tile (8 waves of 64 x 128, as in the dense tile) so each
@@ -124,9 +139,11 @@ constexpr int kGroupedBN = 256;
 // 160- and 192-row tiles hold experts of 129..192 rows: their waves take 48
 // rows each, so for up to 144 rows the fourth row of waves has none and
 // skips its MFMAs (64-row waves would run three full waves for 129 rows).
-template <int ROWS, int S>
+// CAST: 0, or 1 + the scale mode of activations quantized inside the GEMM
+// (the same LDS ring: the cast writes the codes where the loads would).
+template <int ROWS, int S, int CAST = 0>
 using GroupedCfg =
-    GemmCfg<(ROWS == 160 || ROWS == 192 ? 192 : 256), kGroupedBN, 4, 2, S, ROWS>;
+    GemmCfg<(ROWS == 160 || ROWS == 192 ? 192 : 256), kGroupedBN, 4, 2, S, ROWS, 0, 0, 0, CAST>;
 constexpr int kS64 = 3, kS128 = 3, kS160 = 3, kS192 = 2, kS256 = 2;
 
 // Main-loop schedule constants (measured on the 4096 x 4096 x 7168 shape;
@@ -184,9 +201,9 @@ struct ChunkLoader {
     wave_m = wave_m_;
     const int64_t a_live = t.a_rows - t.a_row0;  // >= 1
     const int64_t w_live = t.w_rows - t.w_row0;  // >= 1
-    ra = make_rsrc(t.A + t.a_row0 * t.K, a_live * t.K);
+    if constexpr (!Cfg::A_CAST) ra = make_rsrc(t.A + t.a_row0 * t.K, a_live * t.K);
     rw = make_rsrc(t.W + t.w_row0 * t.K, w_live * t.K);
-    if constexpr (!Cfg::OP_BF16) {
+    if constexpr (!Cfg::OP_BF16 && !Cfg::A_CAST) {
       const int64_t G = t.K / Cfg::BK;
       rs = make_rsrc(t.SA + t.a_row0, (G * t.sa_ld - t.a_row0) * 4);
       s_stride = t.sa_ld * 4;
@@ -206,7 +223,7 @@ struct ChunkLoader {
     // rows (up to 64; rows past them are loaded and not used), so the scales
     // an MFMA column lane needs (rows c, 16 + c, 32 + c, 48 + c) sit side by
     // side in LDS.
-    if constexpr (!Cfg::OP_BF16) {
+    if constexpr (!Cfg::OP_BF16 && !Cfg::A_CAST) {
       const int64_t rs_row = wave_m_ * Cfg::WM + (lane & 3) * 16 + (lane >> 2);
       voff_s = (uint32_t)((rs_row < a_live ? rs_row : a_live - 1) * 4);
     }
@@ -250,7 +267,7 @@ struct ChunkLoader {
       const int dst = is_a ? m * 1024 : Cfg::A_BYTES + (m - Cfg::A_BLK) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rw, to_lds(stage + dst), 16, voff[d],
                                                (int)(g * Cfg::BK), 0, 0);
-    } else if (!Cfg::OP_BF16 && d == Cfg::PER_WAVE) {
+    } else if (!Cfg::OP_BF16 && !Cfg::A_CAST && d == Cfg::PER_WAVE) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave_m * 256), 4, voff_s,
           (int)(g * s_stride), 0, 0);
@@ -260,6 +277,100 @@ struct ChunkLoader {
           to_lds(stage + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::SA_BYTES + (wave % 4) * 256), 4,
           voff_sb, (int)(g * sb_stride), 0, 0);
     }
+  }
+};
+
+// The activation operand quantized on its way into LDS: the FP8 cast fused
+// with the global-to-LDS transfer (why-be.co.kr as_center post 57820,
+// hardware-suggestion passage: the cast done during the transfer instead of
+// an HBM round trip of the codes).  Each K chunk of the tile's BF16 rows
+// comes into registers, 8 lanes per row (16 values, 32 bytes each) and 64
+// rows per round (few registers: the main loop holds 221 of the 256).  The
+// lanes of a row reduce its 1x128 group max-abs over their 8 (DPP), apply the quantizer's rule (quant_rules.hpp: the same
+// codes and scale as fp8q_quantize_act, bit for bit), and write the codes into
+// the stage's A slot at the swizzled places the direct loads would fill, and
+// the scale into the row-scale slot of the row's wave row.  Rows past the
+// valid range are read from the last valid row, as in the loads (their
+// results are never stored).  The code has no branch: lanes past the staged
+// rows (a partial last round) redo the last staged row and write the same
+// bytes to the same places, and the 8 lanes of a row all write its scale.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
+
+// Max-abs of 16 BF16 values as BF16 magnitude bits (in the low half), by
+// packed 16-bit integer max: for non-negative floats the integer order of the
+// bit patterns is the numeric order, so this is exactly the max of |x|.
+__device__ __forceinline__ uint32_t absmax16_bits(const uint4& p, const uint4& q) {
+  const uint32_t m = 0x7FFF7FFFu;
+  auto h = [](uint32_t w) { return __builtin_bit_cast(v2u16, w); };
+  v2u16 r = __builtin_elementwise_max(h(p.x & m), h(p.y & m));
+  r = __builtin_elementwise_max(r, __builtin_elementwise_max(h(p.z & m), h(p.w & m)));
+  r = __builtin_elementwise_max(r, __builtin_elementwise_max(h(q.x & m), h(q.y & m)));
+  r = __builtin_elementwise_max(r, __builtin_elementwise_max(h(q.z & m), h(q.w & m)));
+  return r[0] > r[1] ? r[0] : r[1];
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+
+template <class Cfg>
+struct ACaster {
+  static constexpr int R = Cfg::CAST_ROUNDS;
+  __amdgpu_buffer_rsrc_t rx;
+  int a_last;           // last valid row of the tile (only rows below ROWS matter)
+  uint32_t row_bytes;   // 2K
+  int row0;          // this lane's row in round 0 (tid / 8)
+  int oc;            // which 16-value eighth of the row (= logical 16-byte code column)
+  uint4 raw[2];
+
+  // LDS row of this lane in round r.
+  __device__ __forceinline__ int row_of(int r) const {
+    const int row = r * 64 + row0;
+    return row < Cfg::ROWS ? row : Cfg::ROWS - 1;
+  }
+
+  __device__ __forceinline__ void init(const TileArgs& t, int tid) {
+    const int64_t a_live = t.a_rows - t.a_row0;  // >= 1
+    rx = make_rsrc(t.A + t.a_row0 * 2 * t.K, a_live * 2 * t.K);
+    a_last = (int)(a_live < Cfg::ROWS ? a_live - 1 : Cfg::ROWS - 1);
+    row_bytes = (uint32_t)(2 * t.K);
+    row0 = tid >> 3;
+    oc = tid & 7;
+  }
+
+  // BF16 values of chunk g, round r, into registers.
+  __device__ __forceinline__ void load(int64_t g, int r) {
+    const int row = row_of(r);
+    const uint32_t rr = (uint32_t)(row < a_last ? row : a_last);
+    const uint32_t voff = rr * row_bytes + (uint32_t)(oc * 32);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rx, voff + (uint32_t)(16 * p),
+                                                         (int)(g * 256), 0);
+      raw[p] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+
+  // Codes and scale of the loaded round r into `stage`.
+  __device__ __forceinline__ void cast_store(uint8_t* stage, int r) const {
+    uint32_t ab = absmax16_bits(raw[0], raw[1]);
+    ab = dpp_umax<kDppQuadXor1>(ab);       // the 8 lanes of a row: two quads,
+    ab = dpp_umax<kDppQuadXor2>(ab);
+    ab = dpp_umax<kDppRowHalfMirror>(ab);  // then each quad against the other
+    const GroupRule rule = group_rule<Cfg::CAST_MODE>(__uint_as_float(ab << 16));
+    const uint2 c0 = convert8<Cfg::CAST_MODE>(raw[0], rule);
+    const uint2 c1 = convert8<Cfg::CAST_MODE>(raw[1], rule);
+    const int row = row_of(r);
+    // K bytes 16oc .. 16oc+15 of the row: logical 16-byte column oc.
+    *reinterpret_cast<v4u*>(stage + row * 128 + swz(row, oc) * 16) = v4u{c0.x, c0.y, c1.x, c1.y};
+    // Slot position of row rr of a wave row: (rr % 16) * 4 + rr / 16, the
+    // order the scale loads of the other configurations produce.
+    const int wm = row / Cfg::WM, rr = row % Cfg::WM;
+    *reinterpret_cast<float*>(stage + Cfg::A_BYTES + Cfg::B_BYTES + wm * 256 +
+                              ((rr & 15) * 4 + (rr >> 4)) * 4) = rule.s;
   }
 };
 
@@ -343,7 +454,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
   // activation blocks, then h = 1, so chained MFMAs are MB steps apart.
   // The matrix core therefore never waits for a chunk boundary: a wave that
   // arrives early at the barrier leaves the matrix core to its SIMD partner.
-  constexpr int LAG = Cfg::OP_BF16 ? 0 : kPromoteLag;
+  // (Lag 1 with the activation cast: its registers come out of the partials'.)
+  constexpr int LAG = Cfg::OP_BF16 ? 0 : Cfg::A_CAST ? 1 : kPromoteLag;
   constexpr int KSTEPS = RB * NB + LAG;
   constexpr int kBar = RB * (NB - 1) - kBarLead;   // before the last row block
   constexpr int TAIL = KSTEPS - 1 - kBar;          // loads issued after the barrier
@@ -370,8 +482,27 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
                     kPfAt + (Cfg::PF_LOADS - 1) * kDmaStep < kBar,
                 "prefetches go out after the head loads and before the barrier");
 
+  // Activation cast: round r of chunk g+1 is quantized into chunk g+1's stage
+  // at step cast_step(r) of chunk g, the last a few steps before the barrier
+  // that publishes chunk g+1.  Round 0's BF16 values are loaded right after
+  // chunk g-1's barrier, ahead of the operand loads issued there, and round
+  // r+1's right after round r's cast (one register set: a second one spills
+  // the main loop), so each load has the steps up to its cast to arrive; the
+  // casts are spread evenly over the chunk's cycle.  The stage of chunk g+1 is
+  // free from chunk g's start on: its last reader, chunk g+1-S, ended before
+  // chunk g-1's barrier.
+  constexpr int CR = Cfg::CAST_ROUNDS;
+  constexpr int kCastLast = kBar - 3;
+  constexpr int kCastGap =
+      CR > 1 ? (kCastLast / (CR - 1) < KSTEPS / CR ? kCastLast / (CR - 1) : KSTEPS / CR) : 0;
+  auto cast_step = [](int r) constexpr { return kCastLast - (CR - 1 - r) * kCastGap; };
+  static_assert(CR == 0 || (cast_step(0) >= 0 && kBar + 1 < KSTEPS),
+                "the casts of a chunk precede its barrier");
+
   ChunkLoader<Cfg> ld;
   ld.init(t, wave, wave_m, lane);
+  ACaster<Cfg> cs;
+  if constexpr (Cfg::A_CAST) cs.init(t, threadIdx.x);
   // Chunk indices past the end are clamped to the last chunk: the extra loads
   // re-fetch L2-resident bytes into a stage nobody reads again, and keep the
   // number of loads in flight the same every iteration.
@@ -397,8 +528,16 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
 #pragma unroll
   for (int d = 0; d < D1; ++d)
     ld.issue(smem + (S - 1) * Cfg::STAGE, S - 1 < g_last ? S - 1 : g_last, d);
+  if constexpr (Cfg::A_CAST) {
+#pragma unroll
+    for (int r = 0; r < CR; ++r) {
+      cs.load(0, r);
+      cs.cast_store(smem, r);
+    }
+  }
   wait_vmcnt<kAfter + D1>();  // chunk 0 landed
   lds_barrier();
+  if constexpr (Cfg::A_CAST) cs.load(g_last > 0 ? 1 : 0, 0);
 
   v8i a[MB];     // activation fragments of the chunk (MFMA B operand)
   v8i b[NBUF];   // weight fragments, a ring over row blocks (MFMA A operand)
@@ -417,6 +556,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
     const int64_t g_head = g + S - 1 < g_last ? g + S - 1 : g_last;
     const int64_t g_tail = g + S < g_last ? g + S : g_last;
     const int64_t g_pf = g + kPfDist < g_last ? g + kPfDist : g_last;
+    const int64_t g_nxt = g + 1 < g_last ? g + 1 : g_last;
+    const int64_t g_nxt2 = g + 2 < g_last ? g + 2 : g_last;
     uint8_t* const st_cur = smem + cur * Cfg::STAGE;
     uint8_t* const st_nxt = smem + nxt * Cfg::STAGE;
     uint8_t* const st_head = smem + head * Cfg::STAGE;
@@ -425,8 +566,16 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
       for (int d = D1; d < Cfg::LOADS; ++d) ld.issue(st_head, g_head, d);
 #pragma unroll
       for (int h = 0; h < PFL; ++h) ld.prefetch(pf_slot, g_pf, h);
+      if constexpr (Cfg::A_CAST) {
+#pragma unroll
+        for (int r = 0; r < CR; ++r) {
+          cs.cast_store(st_nxt, r);
+          if (r + 1 < CR) cs.load(g_nxt, r + 1);
+        }
+      }
       wait_vmcnt<kAfter>();
       lds_barrier();
+      if constexpr (Cfg::A_CAST) cs.load(g_nxt2, 0);
 #pragma unroll
       for (int d = 0; d < D1; ++d) ld.issue(st_cur, g_tail, d);
       cur = nxt;
@@ -497,6 +646,10 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
           if (k == next_b_step(t))
             b[t] = load_frag(st_nxt + Cfg::A_BYTES, wave_n * Cfg::WN + t * 16 + r16, q);
       }
+      // (Issued before the tail loads, so that waiting for these BF16
+      // values never waits for chunk g+S's operands.)
+      if constexpr (Cfg::A_CAST)
+        if (k == kBar + 1) cs.load(g_nxt2, 0);
 #pragma unroll
       for (int d = 0; d < D1; ++d)
         if (k == kBar + 1 + d) ld.issue(st_cur, g_tail, d);
@@ -514,6 +667,15 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
         if (kp >= 0) promote(acc[kp % MB][kp / MB], p[kp % (LAG + 1)], mult[kp % MB]);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (Cfg::A_CAST) {
+#pragma unroll
+        for (int r = 0; r < CR; ++r)
+          if (k == cast_step(r)) {
+            cs.cast_store(st_nxt, r);
+            if (r + 1 < CR) cs.load(g_nxt, r + 1);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     cur = nxt;
   }
@@ -605,6 +767,9 @@ static_assert(GroupedCfg<64, kS64>::THREADS == kGroupedThreads &&
                   GroupedCfg<256, kS256>::THREADS == kGroupedThreads,
               "all grouped configurations use the same workgroup");
 
+// CAST: 0 = FP8 activation codes and scales in A / SA; 1 + scale mode = BF16
+// activations in A (SA unused), quantized inside the tiles.
+template <int CAST>
 __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ SA, int64_t M_total,
     const int32_t* __restrict__ off, int G, const uint8_t* __restrict__ W,
@@ -742,15 +907,15 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
     t.out_bf16 = out_bf16;
     const int64_t live = r1 - t.a_row0;  // 1 .. (>= 256 when more m-tiles follow)
     if (live <= 64)
-      gemm_tile<GroupedCfg<64, kS64>>(t, smem);
+      gemm_tile<GroupedCfg<64, kS64, CAST>>(t, smem);
     else if (live <= 128)
-      gemm_tile<GroupedCfg<128, kS128>>(t, smem);
+      gemm_tile<GroupedCfg<128, kS128, CAST>>(t, smem);
     else if (live <= 160)
-      gemm_tile<GroupedCfg<160, kS160>>(t, smem);
+      gemm_tile<GroupedCfg<160, kS160, CAST>>(t, smem);
     else if (live <= 192)
-      gemm_tile<GroupedCfg<192, kS192>>(t, smem);
+      gemm_tile<GroupedCfg<192, kS192, CAST>>(t, smem);
     else
-      gemm_tile<GroupedCfg<256, kS256>>(t, smem);
+      gemm_tile<GroupedCfg<256, kS256, CAST>>(t, smem);
     __syncthreads();  // the next tile's loads reuse the ring
   }
 }
@@ -798,10 +963,30 @@ hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
-                               const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
-                               int64_t N, int64_t K, void* c, int out_bf16,
-                               hipStream_t stream) {
+// BF16 activations x quantized inside the dense GEMM (scale mode `mode`).
+hipError_t launch_gemm_cast(const void* x, const uint8_t* w_q, const float* w_s, int64_t M,
+                            int64_t N, int64_t K, void* c, int out_bf16, int mode,
+                            hipStream_t stream) {
+  using Cfg = DenseCastCfg<0>;
+  static_assert(DenseCastCfg<1>::BM == Cfg::BM && DenseCastCfg<1>::BN == Cfg::BN, "same tiles");
+  if (M == 0 || N == 0) return hipSuccess;
+  const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+  const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  auto kern = mode == 0 ? gemm_kernel<DenseCastCfg<0>> : gemm_kernel<DenseCastCfg<1>>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream,
+                     static_cast<const uint8_t*>(x), nullptr, w_q, w_s, M, N, K, c, out_bf16,
+                     (int)tiles_n);
+  return hipGetLastError();
+}
+
+// cast = 0: a holds FP8 codes with scales a_s; cast = 1 + mode: a holds BF16
+// activations quantized inside the kernel (a_s unused).
+static hipError_t launch_grouped(const uint8_t* a, const float* a_s, int64_t M_total,
+                                 const int32_t* off, int G, const uint8_t* w_q,
+                                 const float* w_s, int64_t N, int64_t K, void* c, int out_bf16,
+                                 int cast, hipStream_t stream) {
   if (M_total == 0 || N == 0) return hipSuccess;
   if (G > kMaxExpertsLds) return hipErrorInvalidValue;
   const int64_t tiles_n = (N + kGroupedBN - 1) / kGroupedBN;
@@ -821,10 +1006,26 @@ hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_t
   if (k8 < (per_xcd + 63) / 64) k8 = (per_xcd + 63) / 64;
   const int64_t grid = k8 * kXcds;
   // The largest-first order applies up to 4 tiles per CU of the device.
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)grid), dim3(kGroupedThreads), 0,
-                     stream, a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16,
-                     (int)tiles_n, 4 * cus);
+  auto kern = cast == 0   ? grouped_gemm_kernel<0>
+              : cast == 1 ? grouped_gemm_kernel<1>
+                          : grouped_gemm_kernel<2>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kGroupedThreads), 0, stream, a, a_s,
+                     M_total, off, G, w_q, w_s, N, K, c, out_bf16, (int)tiles_n, 4 * cus);
   return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                               const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
+                               int64_t N, int64_t K, void* c, int out_bf16,
+                               hipStream_t stream) {
+  return launch_grouped(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out_bf16, 0, stream);
+}
+
+hipError_t launch_grouped_gemm_cast(const void* x, int64_t M_total, const int32_t* off, int G,
+                                    const uint8_t* w_q, const float* w_s, int64_t N, int64_t K,
+                                    void* c, int out_bf16, int mode, hipStream_t stream) {
+  return launch_grouped(static_cast<const uint8_t*>(x), nullptr, M_total, off, G, w_q, w_s, N,
+                        K, c, out_bf16, 1 + mode, stream);
 }
 
 }  // namespace fp8q

@@ -12,78 +12,13 @@
 // for activations, plus LDS across waves for weight blocks), and the codes are
 // written with 8-byte non-temporal stores, 128 contiguous bytes per group row.
 //
-// Arithmetic (bit-exact contract): FP32 mode computes inv = 448/amax and
-// s = amax/448 with IEEE-correct division (this file is built without fast
-// math and without FP contraction), then code = cvt_e4m3_rne(x * inv).  A
-// non-finite inv flushes the group: s = 0 and x * 0 = signed zero.  Pow2 mode
-// scales by an exact ldexp.
+// Arithmetic (bit-exact contract): the group rule and conversion in
+// quant_rules.hpp; this file is built without fast math and without FP
+// contraction.
 
-#include "fp8q_device.hpp"
+#include "quant_rules.hpp"
 
 namespace fp8q {
-
-struct GroupRule {
-  float mul;   // FP32 mode: x * mul
-  int neg_e;   // pow2 mode: ldexp(x, neg_e)
-  float s;     // stored dequantization scale
-};
-
-// Smallest e with 448 * 2^e >= a (a > 0, finite), from the bits of a.
-// a = f * 2^E with f in [1, 2); 448 = 1.75 * 2^8, so e = E - 8 if f <= 1.75
-// and e = E - 7 otherwise.
-__device__ __forceinline__ int pow2_exponent(float a) {
-  const uint32_t b = __float_as_uint(a);
-  const int ef = (int)(b >> 23);
-  uint32_t man = b & 0x7FFFFFu;
-  int E;
-  if (ef != 0) {
-    E = ef - 127;
-  } else {  // FP32 subnormal (a BF16 subnormal widened): a = man * 2^-149
-    const int p = 31 - __clz(man);
-    E = p - 149;
-    man = (man << (23 - p)) & 0x7FFFFFu;
-  }
-  return (man <= 0x600000u) ? E - 8 : E - 7;
-}
-
-__device__ __forceinline__ float exp2_int(int e) {  // 2^e for e in [-149, 127]
-  return (e >= -126) ? __uint_as_float((uint32_t)(e + 127) << 23)
-                     : __uint_as_float(1u << (e + 149));
-}
-
-template <int MODE>
-__device__ __forceinline__ GroupRule group_rule(float amax) {
-  GroupRule r;
-  if (MODE == 0) {
-    const float inv = kE4M3Max / amax;
-    const bool flushed = !__builtin_isfinite(inv);
-    r.mul = flushed ? 0.0f : inv;
-    r.s = flushed ? 0.0f : amax / kE4M3Max;
-    r.neg_e = 0;
-  } else {
-    const int e = (amax > 0.0f) ? pow2_exponent(amax) : 0;
-    r.neg_e = -e;
-    r.s = (amax > 0.0f) ? exp2_int(e) : 0.0f;
-    r.mul = 0.0f;
-  }
-  return r;
-}
-
-template <int MODE>
-__device__ __forceinline__ float apply(float x, const GroupRule& r) {
-  return MODE == 0 ? x * r.mul : __builtin_ldexpf(x, r.neg_e);
-}
-
-// 8 BF16 values (one 16-byte load) -> 8 E4M3 bytes.
-template <int MODE>
-__device__ __forceinline__ uint2 convert8(const uint4 v, const GroupRule& r) {
-  uint2 o;
-  o.x = pack_e4m3x4(apply<MODE>(bf16_lo(v.x), r), apply<MODE>(bf16_hi(v.x), r),
-                    apply<MODE>(bf16_lo(v.y), r), apply<MODE>(bf16_hi(v.y), r));
-  o.y = pack_e4m3x4(apply<MODE>(bf16_lo(v.z), r), apply<MODE>(bf16_hi(v.z), r),
-                    apply<MODE>(bf16_lo(v.w), r), apply<MODE>(bf16_hi(v.w), r));
-  return o;
-}
 
 // 8 code bytes, stored non-temporally: the codes are read back by a GEMM
 // launch later, not by this one, so they need not displace cached lines on the
@@ -93,17 +28,6 @@ __device__ __forceinline__ uint2 convert8(const uint4 v, const GroupRule& r) {
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store_codes(uint8_t* dst, const uint2 o) {
   __builtin_nontemporal_store(v2u{o.x, o.y}, reinterpret_cast<v2u*>(dst));
-}
-
-__device__ __forceinline__ float absmax8(const uint4 v) {
-  // |bf16| as float: clear the sign bits, then widen.
-  const uint32_t m = 0x7FFF7FFFu;
-  const uint32_t a = v.x & m, b = v.y & m, c = v.z & m, d = v.w & m;
-  float r = fmaxf(bf16_lo(a), bf16_hi(a));
-  r = fmaxf(r, fmaxf(bf16_lo(b), bf16_hi(b)));
-  r = fmaxf(r, fmaxf(bf16_lo(c), bf16_hi(c)));
-  r = fmaxf(r, fmaxf(bf16_lo(d), bf16_hi(d)));
-  return r;
 }
 
 // ---------------------------------------------------------------------------

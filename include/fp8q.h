@@ -221,6 +221,35 @@ fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s,
 fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
                            void* c, fp8q_out_dtype out, hipStream_t stream);
 
+/*
+ * GEMMs that quantize their BF16 activation operand themselves: the FP8 cast
+ * fused with the transfer of the activations into on-chip memory, instead of
+ * writing the codes to HBM and reading them back (why-be.co.kr as_center post
+ * 57820, hardware-suggestion passage; the-good.kr post 2169793, fine-grained
+ * quantization passage).  Every K chunk of a tile's activation rows is
+ * quantized by the rule of fp8q_quantize_act with scale mode `mode`, so
+ *   fp8q_gemm_fused(x, w_q, w_s, ...) == fp8q_gemm(fp8q_quantize_act(x, mode), w_q, w_s, ...)
+ * bit for bit, and likewise the grouped call against fp8q_grouped_gemm.  The
+ * codes and scales of x are not written out.  Each tile re-quantizes its rows
+ * (once per 256 output columns).
+ *   x_bf16 : [M][K] (or [M_total][K]) bfloat16, row-major; 16-byte aligned.
+ *   w_q, w_s, off, c, out and the shape rules: as fp8q_gemm / fp8q_grouped_gemm.
+ * FP8Q_ERR_UNSUPPORTED: K == 0 with output rows, K > 2^21 (32-bit load
+ *   offsets over rows of 2K bytes), or (grouped) G > 1024.
+ * Accuracy as fp8q_gemm (the same arithmetic on the same codes).
+ */
+fp8q_status fp8q_gemm_fused(const void* x_bf16, const uint8_t* w_q, const float* w_s,
+                            int64_t M, int64_t N, int64_t K,
+                            void* c, fp8q_out_dtype out, fp8q_scale_mode mode,
+                            hipStream_t stream);
+
+fp8q_status fp8q_grouped_gemm_fused(const void* x_bf16, int64_t M_total,
+                                    const int32_t* off, int32_t G,
+                                    const uint8_t* w_q, const float* w_s,
+                                    int64_t N, int64_t K,
+                                    void* c, fp8q_out_dtype out, fp8q_scale_mode mode,
+                                    hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fp8q_status_string(fp8q_status status);
 

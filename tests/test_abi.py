@@ -35,6 +35,8 @@ def lib():
     L.fp8q_quantize_act_t.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_quantize_weight_t.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_gemm_rowscaled.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
+    L.fp8q_gemm_fused.argtypes = [p, p, p, i64, i64, i64, p, i32, i32, p]
+    L.fp8q_grouped_gemm_fused.argtypes = [p, i64, p, i32, p, p, i64, i64, p, i32, i32, p]
     L.fp8q_status_string.restype = ctypes.c_char_p
     L.fp8q_status_string.argtypes = [ctypes.c_int]
     return L
@@ -51,7 +53,8 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm",
                           "fp8q_grouped_gemm", "fp8q_gemm_bf16", "fp8q_quantize_act_t",
-                          "fp8q_quantize_weight_t", "fp8q_gemm_rowscaled", "fp8q_status_string",
+                          "fp8q_quantize_weight_t", "fp8q_gemm_rowscaled", "fp8q_gemm_fused",
+                          "fp8q_grouped_gemm_fused", "fp8q_status_string",
                           "fp8q_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -175,6 +178,44 @@ def test_gemm_rowscaled_validation(lib):
     assert f(A, A, A, A, 4, 1 << 29, 128, A, 0, None) == E_UNSUP    # b_s offsets >= 2^31
 
 
+def test_gemm_fused_validation(lib):
+    f = lib.fp8q_gemm_fused
+    assert f(A, A, A, 4, 128, 128, None, 0, 0, None) == E_NULL
+    assert f(None, A, A, 4, 128, 128, A, 0, 0, None) == E_NULL
+    assert f(A, None, A, 4, 128, 128, A, 0, 0, None) == E_NULL
+    assert f(A, A, None, 4, 128, 128, A, 0, 0, None) == E_NULL
+    assert f(A, A, A, 4, 100, 128, A, 0, 0, None) == E_SHAPE
+    assert f(A, A, A, 4, 128, 64, A, 0, 0, None) == E_SHAPE
+    assert f(A, A, A, -4, 128, 128, A, 0, 0, None) == E_SHAPE
+    assert f(A + 2, A, A, 4, 128, 128, A, 0, 0, None) == E_ALIGN
+    assert f(A, A + 8, A, 4, 128, 128, A, 0, 0, None) == E_ALIGN
+    assert f(A, A, A + 2, 4, 128, 128, A, 0, 0, None) == E_ALIGN
+    assert f(A, A, A, 4, 128, 128, A + 4, 0, 0, None) == E_ALIGN
+    assert f(A, A, A, 4, 128, 128, A, 2, 0, None) == E_ENUM       # out dtype
+    assert f(A, A, A, 4, 128, 128, A, 0, 2, None) == E_ENUM       # scale mode
+    assert f(None, None, None, 0, 128, 128, None, 0, 0, None) == OK
+    assert f(A, A, A, 4, 128, 0, A, 0, 0, None) == E_UNSUP
+    assert f(A, A, A, 4, 128, (1 << 21) + 128, A, 0, 0, None) == E_UNSUP
+
+
+def test_grouped_gemm_fused_validation(lib):
+    f = lib.fp8q_grouped_gemm_fused
+    assert f(A, 8, None, 2, A, A, 128, 128, A, 0, 0, None) == E_NULL
+    assert f(A, 8, A, 2, A, A, 128, 128, None, 0, 0, None) == E_NULL
+    assert f(None, 8, A, 2, A, A, 128, 128, A, 0, 0, None) == E_NULL
+    assert f(A, 8, A, 0, A, A, 128, 128, A, 0, 0, None) == E_SHAPE
+    assert f(A, 8, A, 2, A, A, 200, 128, A, 0, 0, None) == E_SHAPE
+    assert f(A, -8, A, 2, A, A, 128, 128, A, 0, 0, None) == E_SHAPE
+    assert f(A, 8, A + 2, 2, A, A, 128, 128, A, 0, 0, None) == E_ALIGN
+    assert f(A + 8, 8, A, 2, A, A, 128, 128, A, 0, 0, None) == E_ALIGN
+    assert f(A, 8, A, 2, A, A, 128, 128, A, 5, 0, None) == E_ENUM
+    assert f(A, 8, A, 2, A, A, 128, 128, A, 0, 7, None) == E_ENUM
+    assert f(A, 8, A, 2000, A, A, 128, 128, A, 0, 0, None) == E_UNSUP
+    assert f(A, 8, A, 2, A, A, 128, 0, A, 0, 0, None) == E_UNSUP
+    assert f(A, 8, A, 2, A, A, 128, (1 << 21) + 128, A, 0, 0, None) == E_UNSUP
+    assert f(None, 0, A, 2, None, None, 128, 128, None, 0, 0, None) == OK
+
+
 def test_valid_arguments_without_gpu_report_device_error(lib):
     if not _no_device():
         pytest.skip("a GPU is visible: fake pointers must not be launched")
@@ -186,3 +227,5 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert lib.fp8q_quantize_act_t(A, 128, 128, A, A, 0, None) == E_DEVICE
     assert lib.fp8q_quantize_weight_t(A, 128, 128, A, A, 0, None) == E_DEVICE
     assert lib.fp8q_gemm_rowscaled(A, A, A, A, 4, 128, 128, A, 0, None) == E_DEVICE
+    assert lib.fp8q_gemm_fused(A, A, A, 4, 128, 128, A, 0, 1, None) == E_DEVICE
+    assert lib.fp8q_grouped_gemm_fused(A, 8, A, 2, A, A, 128, 128, A, 0, 0, None) == E_DEVICE
