@@ -53,10 +53,13 @@ def _weights(N, K, seed, mode="f32", G=None):
     return W, wq, ws
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (17, 384, 640), (255, 256, 256),
-                                   (300, 512, 1152), (513, 640, 384), (64, 128, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 128), (2, 256, 256), (129, 128, 384), (17, 384, 640),
+                                   (255, 256, 256), (300, 512, 1152), (513, 640, 384),
+                                   (64, 128, 2048)])
 @pytest.mark.parametrize("mode", ["f32", "pow2"])
 def test_gemm_fused_equals_quantize_then_gemm(M, N, K, mode):
+    """K = 128 and 256 take the paths where the chunk after next is clamped
+    to the last chunk."""
     f = fq()
     X = _special(M, K, M * 3 + N + K)
     _, wq, ws = _weights(N, K, N + K, mode)
@@ -178,3 +181,16 @@ def test_grouped_fused_decode_workload_full_size():
     c_ref = f.grouped_gemm(aq, as_, d_off, wq, ws, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     _same(c, c_ref, "decode workload")
+
+
+def test_grouped_fused_many_experts():
+    """1024 experts (the limit), most of them empty, the others 1..70 rows;
+    one K chunk (K = 128), so every cast load past the first chunk is clamped."""
+    rng = np.random.default_rng(1024)
+    G = 1024
+    counts = np.where(rng.random(G) < 0.08, rng.integers(1, 71, G), 0)
+    counts[0], counts[-1], counts[511], counts[512] = 3, 65, 1, 64
+    X, Wst, off, c, c_ref = _grouped(list(counts), 128, 128, 51, "f32", extra_rows=3)
+    n = int(off[-1])
+    _same(c[:n], c_ref[:n], "1024 experts")
+    assert torch.isnan(c[n:]).all(), "rows past off[G] must be left untouched"
