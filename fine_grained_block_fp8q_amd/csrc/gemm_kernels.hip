@@ -32,12 +32,13 @@
 // prefetch several chunks ahead, split between the tiles that share a band
 // of A or W rows in one XCD's L2.
 //
-// The same tile serves three more configurations (GemmCfg flags): the
+// The same tile serves four more configurations (GemmCfg flags): the
 // weight-gradient GEMM, whose weight-side operand carries 1x128 row-group
 // scales like the activations (W_ROWSCALE: the multiplier differs per output
 // element); BF16 operands without scales (OP_BF16: the reference of the FP8
-// path, accumulating in the matrix core); and the grouped MoE kernel's
-// row-count buckets (persistent workgroups, see grouped_gemm_kernel).
+// path, accumulating in the matrix core); BF16 activations quantized on their
+// way into LDS (A_CAST, see ACaster); and the grouped MoE kernel's row-count
+// buckets (persistent workgroups, see grouped_gemm_kernel).
 
 #include "gemm_common.hpp"
 #include "quant_rules.hpp"
@@ -318,13 +319,12 @@ __device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
 
 template <class Cfg>
 struct ACaster {
-  static constexpr int R = Cfg::CAST_ROUNDS;
-  __amdgpu_buffer_rsrc_t rx;
-  int a_last;           // last valid row of the tile (only rows below ROWS matter)
-  uint32_t row_bytes;   // 2K
-  int row0;          // this lane's row in round 0 (tid / 8)
-  int oc;            // which 16-value eighth of the row (= logical 16-byte code column)
-  uint4 raw[2];
+  __amdgpu_buffer_rsrc_t rx;  // the tile's BF16 rows
+  int a_last;                 // last valid row of the tile (only rows below ROWS matter)
+  uint32_t row_bytes;         // 2K
+  int row0;                   // this lane's row in round 0 (tid / 8)
+  int oc;                     // which 16-value eighth of the row (= logical code column)
+  uint4 raw[2];               // the loaded round's 16 BF16 values
 
   // LDS row of this lane in round r.
   __device__ __forceinline__ int row_of(int r) const {
