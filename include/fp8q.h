@@ -227,7 +227,8 @@ fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, i
  * writing the codes to HBM and reading them back (why-be.co.kr as_center post
  * 57820, hardware-suggestion passage; the-good.kr post 2169793, fine-grained
  * quantization passage).  Every K chunk of a tile's activation rows is
- * quantized by the rule of fp8q_quantize_act with scale mode `mode`, so
+ * quantized by the rule of fp8q_quantize_act with scale mode `mode`, so, for
+ * finite inputs (the contract of every call),
  *   fp8q_gemm_fused(x, w_q, w_s, ...) == fp8q_gemm(fp8q_quantize_act(x, mode), w_q, w_s, ...)
  * bit for bit, and likewise the grouped call against fp8q_grouped_gemm.  The
  * codes and scales of x are not written out.  Each tile re-quantizes its rows
