@@ -105,6 +105,25 @@ def test_act_exhaustive_bf16_values(amax_bits):
         _assert_same(gq, gs, rq, rs, f"act exhaustive amax={amax_bits:#06x} {mode}")
 
 
+def test_act_every_bf16_group_max():
+    """One group per positive finite BF16 value a (32,639 groups: every
+    subnormal and normal magnitude), holding a, -a and zeros: the scale rule
+    of both modes, including the exponent of subnormal maxima in the pow2
+    mode, is checked for every possible group max."""
+    a = np.arange(1, 0x7F80, dtype=np.uint16)          # 0x0001 .. 0x7F7F
+    groups = np.zeros((len(a), 128), np.uint16)
+    groups[:, 0] = a
+    groups[:, 1] = a | 0x8000
+    G = 8
+    pad = (-len(a)) % G
+    groups = np.concatenate([groups, np.zeros((pad, 128), np.uint16)])
+    bits = groups.reshape(-1, G * 128)
+    for mode in ("f32", "pow2"):
+        gq, gs = _gpu_act(bits, mode)
+        rq, rs = oquant.quantize_act(bits, mode)
+        _assert_same(gq, gs, rq, rs, f"act every group max {mode}")
+
+
 def test_act_random_bit_patterns():
     rng = np.random.default_rng(99)
     bits = rng.integers(0, 65536, size=(257, 1024), dtype=np.uint64).astype(np.uint16)
