@@ -194,3 +194,28 @@ def test_grouped_fused_many_experts():
     n = int(off[-1])
     _same(c[:n], c_ref[:n], "1024 experts")
     assert torch.isnan(c[n:]).all(), "rows past off[G] must be left untouched"
+
+
+@pytest.mark.parametrize("mode", ["f32", "pow2"])
+def test_gemm_fused_every_bf16_group_max(mode):
+    """One activation group per positive finite BF16 value a (every subnormal
+    and normal magnitude), holding a, -a/2 and small values: the fused cast's
+    scale and codes for every possible group max, through the GEMM output,
+    bitwise against quantize-then-GEMM."""
+    a = np.arange(1, 0x7F80, dtype=np.uint16)
+    groups = np.zeros((len(a), 128), np.uint16)
+    groups[:, 0] = a
+    groups[:, 1] = workloads.bf16_bits(-0.5 * oquant.bf16_bits_to_f32(a))
+    groups[:, 2] = a >> 1  # a smaller positive bit pattern, so a smaller magnitude
+    G = 8
+    pad = (-len(a)) % G
+    groups = np.concatenate([groups, np.zeros((pad, 128), np.uint16)])
+    X = groups.reshape(-1, G * 128)
+    f = fq()
+    _, wq, ws = _weights(256, X.shape[1], 7, mode)
+    x = to_dev_bf16(X)
+    c = f.gemm_fused(x, wq, ws, mode)
+    aq, as_ = f.quantize_act(x, mode)
+    c_ref = f.gemm(aq, as_, wq, ws)
+    torch.cuda.synchronize()
+    _same(c, c_ref, f"every group max {mode}")
