@@ -79,7 +79,8 @@ struct GemmCfg {
   static constexpr int A_BYTES = ROWS * BK;
   static constexpr int B_BYTES = BN * BK;
   static constexpr int SA_BYTES = OP_BF16 ? 0 : WAVES_M * 256;  // 64 row scales per row of waves
-  static constexpr int SB_BYTES = W_ROWSCALE ? BN * 4 : 0;        // the tile's weight-row scales
+  // the tile's weight-row scales: 4 slots of 64 (rows past BN loaded, unused)
+  static constexpr int SB_BYTES = W_ROWSCALE ? 4 * 256 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int PF_LOADS = PF_;    // L2 prefetch loads per wave per chunk (0 or 1)
@@ -93,7 +94,8 @@ struct GemmCfg {
       PER_WAVE + (OP_BF16 || A_CAST ? 0 : 1) + (W_ROWSCALE ? 1 : 0);  // + scales
   static constexpr int CAST_ROUNDS = A_CAST ? (ROWS + 63) / 64 : 0;  // 64 rows per round
   static_assert(WM % 16 == 0 && WM <= 64, "a wave's rows fit one 256-byte scale slot");
-  static_assert(128 % WN == 0, "a wave's weight rows lie in one 128-row weight block");
+  static_assert(W_ROWSCALE || 128 % WN == 0,
+                "a wave's weight rows lie in one 128-row weight block (block-scaled weights)");
   // Staged rows: whole 1 KiB loads.  When they stop inside a wave (160 rows
   // in 48-row waves), that wave's fragment reads past them fall inside the
   // stage and feed only rows past the expert's end, which are not stored.
@@ -104,8 +106,8 @@ struct GemmCfg {
   static_assert(PF_LOADS == 0 || (PF_LOADS == 1 && NWAVES >= 2 && ROWS == 256 && BN == 256),
                 "the prefetch share is laid out for 256 x 256 tiles");
   static_assert(LOADS * (STAGES - 1) + PF_LOADS * (STAGES - 1) < 64, "vmcnt range");
-  static_assert(!W_ROWSCALE || (!OP_BF16 && NWAVES == 8 && BN == 256 && WN == 128),
-                "row-scaled weights: 8 waves, each loading 64 of the 256 row scales");
+  static_assert(!W_ROWSCALE || (!OP_BF16 && NWAVES == 8 && WAVES_N == 2 && BN <= 256),
+                "row-scaled weights: 8 waves, each loading 64 of up to 256 row scales");
   static_assert(!A_CAST || (!OP_BF16 && !W_ROWSCALE && PF_LOADS == 0 && THREADS == 512 &&
                             A_CAST_ <= 2 && CAST_ROUNDS <= 4),
                 "activation cast: 512 lanes, 8 per row, FP8 block-scaled weights");
@@ -120,6 +122,12 @@ using DenseCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1>;
 using DenseBf16Cfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 1>;
 // The weight-gradient GEMM: the dense tile with row-scaled weights.
 using RowScaledCfg = GemmCfg<256, 256, 4, 2, 2, 256, 1, 0, 1>;
+// The same with 224-row weight tiles (waves of 64 x 112; row-scaled weights
+// have no 128-row blocks to respect), for shapes where they fill the CUs'
+// rounds better: 4096 x 7168 outputs make 448 tiles of 256 x 256 (a second
+// round 3/4 full on 256 CUs) but 512 of 256 x 224 (two full rounds of
+// 7/8-size tiles).  No L2 prefetch (its share is laid out for 256 x 256).
+using RowScaled224Cfg = GemmCfg<256, 224, 4, 2, 2, 256, 0, 0, 1>;
 // BF16 activations quantized inside the GEMM (scale mode MODE): the dense
 // tile without the L2 prefetch, whose A lines would be BF16 rows.
 template <int MODE>
@@ -935,11 +943,10 @@ hipError_t launch_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
-                                 const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
-                                 int out_bf16, hipStream_t stream) {
-  using Cfg = RowScaledCfg;
-  if (M == 0 || N == 0) return hipSuccess;
+template <class Cfg>
+static hipError_t launch_rowscaled_cfg(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                       const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                       int out_bf16, hipStream_t stream) {
   const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
   const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
   const int64_t tiles = tiles_m * tiles_n;
@@ -947,6 +954,24 @@ hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uin
   hipLaunchKernelGGL(gemm_kernel<Cfg>, dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream, a_q,
                      a_s, b_q, b_s, M, N, K, c, out_bf16, (int)tiles_n);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                 const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                 int out_bf16, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipGetLastError();
+  // Rounds of tiles over the CUs times the tile width: the 224-row weight
+  // tiles when they finish sooner by that measure.
+  const int64_t tm = (M + 255) / 256;
+  const int64_t r256 = (tm * ((N + 255) / 256) + cus - 1) / cus;
+  const int64_t r224 = (tm * ((N + 223) / 224) + cus - 1) / cus;
+  if (r224 * 224 < r256 * 256)
+    return launch_rowscaled_cfg<RowScaled224Cfg>(a_q, a_s, b_q, b_s, M, N, K, c, out_bf16, stream);
+  return launch_rowscaled_cfg<RowScaledCfg>(a_q, a_s, b_q, b_s, M, N, K, c, out_bf16, stream);
 }
 
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,

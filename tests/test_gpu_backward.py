@@ -77,6 +77,28 @@ def test_gemm_rowscaled_parity(M, N, K):
     assert_gemm_close(host(c), oa, osa, ob, osb, what=f"rowscaled {M}x{N}x{K}", rowscaled=True)
 
 
+def test_gemm_rowscaled_both_tile_widths():
+    """The launcher picks 256 x 224 tiles when they fill the CUs' rounds
+    better, else 256 x 256: on 256 CUs a 4096 x 4096 output is one round of
+    256 tiles of 256 x 256 (two of 224), and 4096 x 7168 two rounds either
+    way.  Both outputs are checked on sampled rows, and the narrower tiles'
+    ragged last column tile (7168 = 32 x 224; 4096 = 18 x 224 + 64) too."""
+    rng = np.random.default_rng(31)
+    f = fq()
+    for M, N, K in [(4096, 4096, 256), (4096, 7168, 256), (512, 4096, 384)]:
+        A = _bits(rng.standard_normal((M, K)))
+        B = _bits(rng.standard_normal((N, K)))
+        qa, sa = f.quantize_act(to_dev_bf16(A))
+        qb, sb = f.quantize_act(to_dev_bf16(B))
+        c = f.gemm_rowscaled(qa, sa, qb, sb)
+        torch.cuda.synchronize()
+        rows = np.sort(np.random.default_rng(M + N).choice(M, 8, replace=False))
+        oa, osa = oquant.quantize_act(A[rows])
+        ob, osb = oquant.quantize_act(B)
+        assert_gemm_close(host(c)[rows], oa, osa, ob, osb, model_rows=2, rowscaled=True,
+                          what=f"rowscaled {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_backward_of_a_linear_layer(out):
     """Dgrad and Wgrad of Y = X W^T, each composed from the entry points, against
