@@ -295,12 +295,13 @@ struct ChunkLoader {
 // an HBM round trip of the codes).  Each K chunk of the tile's BF16 rows
 // comes into registers, 8 lanes per row (16 values, 32 bytes each) and 64
 // rows per round (few registers: the main loop holds 221 of the 256).  The
-// lanes of a row reduce its 1x128 group max-abs over their 8 (DPP), apply the quantizer's rule (quant_rules.hpp: the same
-// codes and scale as fp8q_quantize_act, bit for bit), and write the codes into
-// the stage's A slot at the swizzled places the direct loads would fill, and
-// the scale into the row-scale slot of the row's wave row.  Rows past the
-// valid range are read from the last valid row, as in the loads (their
-// results are never stored).  The code has no branch: lanes past the staged
+// 8 lanes of a row reduce its 1x128 group max-abs (DPP), apply the
+// quantizer's rule (quant_rules.hpp: the same codes and scale as
+// fp8q_quantize_act, bit for bit), and write the codes into the stage's A
+// slot at the swizzled places the direct loads would fill, and the scale into
+// the row-scale slot of the row's wave row.  Rows past the valid range are
+// read from the last valid row, as in the loads (their results are never
+// stored).  The code has no branch: lanes past the staged
 // rows (a partial last round) redo the last staged row and write the same
 // bytes to the same places, and the 8 lanes of a row all write its scale.
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -491,8 +492,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& t, uint8_t* smem) {
                 "prefetches go out after the head loads and before the barrier");
 
   // Activation cast: round r of chunk g+1 is quantized into chunk g+1's stage
-  // at step cast_step(r) of chunk g, the last a few steps before the barrier
-  // that publishes chunk g+1.  Round 0's BF16 values are loaded right after
+  // at step cast_step(r) of chunk g, the last one a few steps before the
+  // barrier that publishes chunk g+1.  Round 0's BF16 values are loaded right after
   // chunk g-1's barrier, ahead of the operand loads issued there, and round
   // r+1's right after round r's cast (one register set: a second one spills
   // the main loop), so each load has the steps up to its cast to arrive; the
