@@ -7,9 +7,14 @@ status.  Every step of the computation runs in the HIP kernels of
 libfp8q.so; there is no fallback path -- importing this package without the
 built library raises ImportError.
 
+Before each call the wrappers check on the host what the C ABI cannot see
+(raising ValueError): every tensor's dtype, contiguity and device, and that
+the operand, scale, offset and output shapes agree with each other.  The C
+library then validates sizes, alignment and enums itself.
+
 Allocation helpers (``quantize_act``, ``quantize_weight``, ``gemm``,
-``grouped_gemm``) allocate outputs with torch on the input's device and then
-call the entry points.
+``grouped_gemm``, ...) allocate outputs with torch on the input's device and
+then call the entry points.
 """
 
 import ctypes
@@ -36,8 +41,13 @@ lib.fp8q_quantize_weight.argtypes = [_p, _i64, _i64, _p, _p, _i32, _p]
 lib.fp8q_quantize_weight.restype = _st
 lib.fp8q_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_gemm.restype = _st
+lib.fp8q_gemm_precise.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
+lib.fp8q_gemm_precise.restype = _st
 lib.fp8q_grouped_gemm.argtypes = [_p, _p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32, _p]
 lib.fp8q_grouped_gemm.restype = _st
+lib.fp8q_grouped_gemm_precise.argtypes = [_p, _p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32,
+                                          _p]
+lib.fp8q_grouped_gemm_precise.restype = _st
 lib.fp8q_gemm_bf16.argtypes = [_p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_quantize_act_t.argtypes = [_p, _i64, _i64, _p, _p, _i32, _p]
 lib.fp8q_quantize_act_t.restype = _st
@@ -45,6 +55,8 @@ lib.fp8q_quantize_weight_t.argtypes = [_p, _i64, _i64, _p, _p, _i32, _p]
 lib.fp8q_quantize_weight_t.restype = _st
 lib.fp8q_gemm_rowscaled.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_gemm_rowscaled.restype = _st
+lib.fp8q_gemm_rowscaled_precise.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
+lib.fp8q_gemm_rowscaled_precise.restype = _st
 lib.fp8q_gemm_bf16.restype = _st
 lib.fp8q_gemm_fused.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _i32, _i32, _p]
 lib.fp8q_gemm_fused.restype = _st
@@ -81,6 +93,50 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _dt(name):
+    import torch
+    return {"u8": torch.uint8, "f32": torch.float32, "bf16": torch.bfloat16,
+            "i32": torch.int32}[name]
+
+
+def _req(where, name, t, dtypes, shape, device):
+    """Host-side check of one tensor argument: dtype, contiguity, device, shape."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{where}: {name} must be a torch.Tensor")
+    allowed = [_dt(d) for d in dtypes]
+    if t.dtype not in allowed:
+        raise ValueError(f"{where}: {name} has dtype {t.dtype}, expected one of {allowed}")
+    if not t.is_contiguous():
+        raise ValueError(f"{where}: {name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{where}: {name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dims(where, t, ndim, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != ndim:
+        raise ValueError(f"{where}: {name} must be a {ndim}-d torch.Tensor")
+    return t.shape
+
+
+def _mult128(where, **dims):
+    for k, v in dims.items():
+        if v % GROUP:
+            raise ValueError(f"{where}: {k} = {v} is not a multiple of {GROUP}")
+
+
+def _out_code(where, c):
+    import torch
+    if c.dtype == torch.bfloat16:
+        return OUT_BF16
+    if c.dtype == torch.float32:
+        return OUT_F32
+    raise ValueError(f"{where}: c has dtype {c.dtype}, expected float32 or bfloat16")
+
+
 def _stream(stream, device):
     import torch
     if stream is None:
@@ -95,46 +151,99 @@ def abi_version():
 # ---------------------------------------------------------------- entry points
 def fp8q_quantize_act(x, q, s, mode="f32", stream=None):
     """x: bf16 [M][K] -> q: uint8 [M][K], s: float32 [K/128][M] (in place)."""
-    M, K = x.shape
+    w = "fp8q_quantize_act"
+    M, K = _dims(w, x, 2, "x")
+    _mult128(w, K=K)
+    _req(w, "x", x, ["bf16"], (M, K), x.device)
+    _req(w, "q", q, ["u8"], (M, K), x.device)
+    _req(w, "s", s, ["f32"], (K // GROUP, M), x.device)
     _check(lib.fp8q_quantize_act(_ptr(x), M, K, _ptr(q), _ptr(s), _MODES[mode],
                                  _stream(stream, x.device)), "fp8q_quantize_act")
 
 
 def fp8q_quantize_weight(w, q, s, mode="f32", stream=None):
     """w: bf16 [N][K] -> q: uint8 [N][K], s: float32 [N/128][K/128] (in place)."""
-    N, K = w.shape
+    wh = "fp8q_quantize_weight"
+    N, K = _dims(wh, w, 2, "w")
+    _mult128(wh, N=N, K=K)
+    _req(wh, "w", w, ["bf16"], (N, K), w.device)
+    _req(wh, "q", q, ["u8"], (N, K), w.device)
+    _req(wh, "s", s, ["f32"], (N // GROUP, K // GROUP), w.device)
     _check(lib.fp8q_quantize_weight(_ptr(w), N, K, _ptr(q), _ptr(s), _MODES[mode],
                                     _stream(stream, w.device)), "fp8q_quantize_weight")
 
 
+def _gemm_args(where, a_q, a_s, w_q, w_s, c):
+    M, K = _dims(where, a_q, 2, "a_q")
+    N, _ = _dims(where, w_q, 2, "w_q")
+    _mult128(where, N=N, K=K)
+    dev = a_q.device
+    _req(where, "a_q", a_q, ["u8"], (M, K), dev)
+    _req(where, "a_s", a_s, ["f32"], (K // GROUP, M), dev)
+    _req(where, "w_q", w_q, ["u8"], (N, K), dev)
+    _req(where, "w_s", w_s, ["f32"], (N // GROUP, K // GROUP), dev)
+    _req(where, "c", c, ["f32", "bf16"], (M, N), dev)
+    return M, N, K, _out_code(where, c)
+
+
 def fp8q_gemm(a_q, a_s, w_q, w_s, c, stream=None):
     """c[M][N] (float32 or bfloat16) = block-scaled a_q[M][K] x w_q[N][K]^T."""
-    import torch
-    M, K = a_q.shape
-    N = w_q.shape[0]
-    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    M, N, K, out = _gemm_args("fp8q_gemm", a_q, a_s, w_q, w_s, c)
     _check(lib.fp8q_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
                          _stream(stream, a_q.device)), "fp8q_gemm")
 
 
+def fp8q_gemm_precise(a_q, a_s, w_q, w_s, c, stream=None):
+    """fp8q_gemm with each chunk partial formed by FP16 MFMAs on the widened codes."""
+    M, N, K, out = _gemm_args("fp8q_gemm_precise", a_q, a_s, w_q, w_s, c)
+    _check(lib.fp8q_gemm_precise(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c),
+                                 out, _stream(stream, a_q.device)), "fp8q_gemm_precise")
+
+
+def _grouped_args(where, a_q, a_s, off, w_q, w_s, c):
+    M_total, K = _dims(where, a_q, 2, "a_q")
+    G, N, _ = _dims(where, w_q, 3, "w_q")
+    _mult128(where, N=N, K=K)
+    dev = a_q.device
+    _req(where, "a_q", a_q, ["u8"], (M_total, K), dev)
+    _req(where, "a_s", a_s, ["f32"], (K // GROUP, M_total), dev)
+    _req(where, "off", off, ["i32"], (G + 1,), dev)
+    _req(where, "w_q", w_q, ["u8"], (G, N, K), dev)
+    _req(where, "w_s", w_s, ["f32"], (G, N // GROUP, K // GROUP), dev)
+    _req(where, "c", c, ["f32", "bf16"], (M_total, N), dev)
+    return M_total, G, N, K, _out_code(where, c)
+
+
 def fp8q_grouped_gemm(a_q, a_s, off, w_q, w_s, c, stream=None):
     """Rows [off[e], off[e+1]) of a_q times expert e's w_q[e]; off is a device int32[G+1]."""
-    import torch
-    M_total, K = a_q.shape
-    G, N, _ = w_q.shape
-    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    M_total, G, N, K, out = _grouped_args("fp8q_grouped_gemm", a_q, a_s, off, w_q, w_s, c)
     _check(lib.fp8q_grouped_gemm(_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
                                  _ptr(w_s), N, K, _ptr(c), out, _stream(stream, a_q.device)),
            "fp8q_grouped_gemm")
 
 
+def fp8q_grouped_gemm_precise(a_q, a_s, off, w_q, w_s, c, stream=None):
+    """fp8q_grouped_gemm in the precise mode (FP16 MFMAs on the widened codes)."""
+    M_total, G, N, K, out = _grouped_args("fp8q_grouped_gemm_precise", a_q, a_s, off, w_q, w_s,
+                                          c)
+    _check(lib.fp8q_grouped_gemm_precise(_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
+                                         _ptr(w_s), N, K, _ptr(c), out,
+                                         _stream(stream, a_q.device)),
+           "fp8q_grouped_gemm_precise")
+
+
 def fp8q_gemm_fused(x, w_q, w_s, c, mode="f32", stream=None):
     """c[M][N] = fp8q_gemm(quantize_act(x, mode), w_q, w_s), x: bf16 [M][K]
     quantized inside the GEMM."""
-    import torch
-    M, K = x.shape
-    N = w_q.shape[0]
-    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    wh = "fp8q_gemm_fused"
+    M, K = _dims(wh, x, 2, "x")
+    N, _ = _dims(wh, w_q, 2, "w_q")
+    _mult128(wh, N=N, K=K)
+    _req(wh, "x", x, ["bf16"], (M, K), x.device)
+    _req(wh, "w_q", w_q, ["u8"], (N, K), x.device)
+    _req(wh, "w_s", w_s, ["f32"], (N // GROUP, K // GROUP), x.device)
+    _req(wh, "c", c, ["f32", "bf16"], (M, N), x.device)
+    out = _out_code(wh, c)
     _check(lib.fp8q_gemm_fused(_ptr(x), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
                                _MODES[mode], _stream(stream, x.device)), "fp8q_gemm_fused")
 
@@ -142,10 +251,16 @@ def fp8q_gemm_fused(x, w_q, w_s, c, mode="f32", stream=None):
 def fp8q_grouped_gemm_fused(x, off, w_q, w_s, c, mode="f32", stream=None):
     """The grouped GEMM of quantize_act(x, mode), x: bf16 [M_total][K]
     quantized inside the GEMM; off is a device int32[G+1]."""
-    import torch
-    M_total, K = x.shape
-    G, N, _ = w_q.shape
-    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    wh = "fp8q_grouped_gemm_fused"
+    M_total, K = _dims(wh, x, 2, "x")
+    G, N, _ = _dims(wh, w_q, 3, "w_q")
+    _mult128(wh, N=N, K=K)
+    _req(wh, "x", x, ["bf16"], (M_total, K), x.device)
+    _req(wh, "off", off, ["i32"], (G + 1,), x.device)
+    _req(wh, "w_q", w_q, ["u8"], (G, N, K), x.device)
+    _req(wh, "w_s", w_s, ["f32"], (G, N // GROUP, K // GROUP), x.device)
+    _req(wh, "c", c, ["f32", "bf16"], (M_total, N), x.device)
+    out = _out_code(wh, c)
     _check(lib.fp8q_grouped_gemm_fused(_ptr(x), M_total, _ptr(off), G, _ptr(w_q), _ptr(w_s), N,
                                        K, _ptr(c), out, _MODES[mode],
                                        _stream(stream, x.device)),
@@ -154,36 +269,68 @@ def fp8q_grouped_gemm_fused(x, off, w_q, w_s, c, mode="f32", stream=None):
 
 def fp8q_gemm_bf16(a, w, c, stream=None):
     """c[M][N] (float32 or bfloat16) = a[M][K] x w[N][K]^T, BF16 operands."""
-    import torch
-    M, K = a.shape
-    N = w.shape[0]
-    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    wh = "fp8q_gemm_bf16"
+    M, K = _dims(wh, a, 2, "a")
+    N, _ = _dims(wh, w, 2, "w")
+    _mult128(wh, N=N, K=K)
+    _req(wh, "a", a, ["bf16"], (M, K), a.device)
+    _req(wh, "w", w, ["bf16"], (N, K), a.device)
+    _req(wh, "c", c, ["f32", "bf16"], (M, N), a.device)
+    out = _out_code(wh, c)
     _check(lib.fp8q_gemm_bf16(_ptr(a), _ptr(w), M, N, K, _ptr(c), out, _stream(stream, a.device)),
            "fp8q_gemm_bf16")
 
 
 def fp8q_quantize_act_t(x, q_t, s_t, mode="f32", stream=None):
     """x: bf16 [M][K] -> q_t: uint8 [K][M], s_t: float32 [M/128][K] (in place)."""
-    M, K = x.shape
+    wh = "fp8q_quantize_act_t"
+    M, K = _dims(wh, x, 2, "x")
+    _mult128(wh, M=M, K=K)
+    _req(wh, "x", x, ["bf16"], (M, K), x.device)
+    _req(wh, "q_t", q_t, ["u8"], (K, M), x.device)
+    _req(wh, "s_t", s_t, ["f32"], (M // GROUP, K), x.device)
     _check(lib.fp8q_quantize_act_t(_ptr(x), M, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
                                    _stream(stream, x.device)), "fp8q_quantize_act_t")
 
 
 def fp8q_quantize_weight_t(w, q_t, s_t, mode="f32", stream=None):
     """w: bf16 [N][K] -> q_t: uint8 [K][N], s_t: float32 [K/128][N/128] (in place)."""
-    N, K = w.shape
+    wh = "fp8q_quantize_weight_t"
+    N, K = _dims(wh, w, 2, "w")
+    _mult128(wh, N=N, K=K)
+    _req(wh, "w", w, ["bf16"], (N, K), w.device)
+    _req(wh, "q_t", q_t, ["u8"], (K, N), w.device)
+    _req(wh, "s_t", s_t, ["f32"], (K // GROUP, N // GROUP), w.device)
     _check(lib.fp8q_quantize_weight_t(_ptr(w), N, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
                                       _stream(stream, w.device)), "fp8q_quantize_weight_t")
 
 
+def _rowscaled_args(where, a_q, a_s, b_q, b_s, c):
+    M, K = _dims(where, a_q, 2, "a_q")
+    N, _ = _dims(where, b_q, 2, "b_q")
+    _mult128(where, N=N, K=K)
+    dev = a_q.device
+    _req(where, "a_q", a_q, ["u8"], (M, K), dev)
+    _req(where, "a_s", a_s, ["f32"], (K // GROUP, M), dev)
+    _req(where, "b_q", b_q, ["u8"], (N, K), dev)
+    _req(where, "b_s", b_s, ["f32"], (K // GROUP, N), dev)
+    _req(where, "c", c, ["f32", "bf16"], (M, N), dev)
+    return M, N, K, _out_code(where, c)
+
+
 def fp8q_gemm_rowscaled(a_q, a_s, b_q, b_s, c, stream=None):
     """c[M][N] = a_q[M][K] x b_q[N][K]^T with 1x128 row-group scales on both."""
-    import torch
-    M, K = a_q.shape
-    N = b_q.shape[0]
-    out = OUT_BF16 if c.dtype == torch.bfloat16 else OUT_F32
+    M, N, K, out = _rowscaled_args("fp8q_gemm_rowscaled", a_q, a_s, b_q, b_s, c)
     _check(lib.fp8q_gemm_rowscaled(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K, _ptr(c),
                                    out, _stream(stream, a_q.device)), "fp8q_gemm_rowscaled")
+
+
+def fp8q_gemm_rowscaled_precise(a_q, a_s, b_q, b_s, c, stream=None):
+    """fp8q_gemm_rowscaled in the precise mode (FP16 MFMAs on the widened codes)."""
+    M, N, K, out = _rowscaled_args("fp8q_gemm_rowscaled_precise", a_q, a_s, b_q, b_s, c)
+    _check(lib.fp8q_gemm_rowscaled_precise(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K,
+                                           _ptr(c), out, _stream(stream, a_q.device)),
+           "fp8q_gemm_rowscaled_precise")
 
 
 # ---------------------------------------------------------- allocation helpers
@@ -223,19 +370,21 @@ def quantize_weight_t(w, mode="f32", stream=None):
     return q, s
 
 
-def gemm_rowscaled(a_q, a_s, b_q, b_s, out_dtype=None, stream=None):
+def gemm_rowscaled(a_q, a_s, b_q, b_s, out_dtype=None, stream=None, precise=False):
     import torch
     out_dtype = out_dtype or torch.float32
     c = torch.empty((a_q.shape[0], b_q.shape[0]), dtype=out_dtype, device=a_q.device)
-    fp8q_gemm_rowscaled(a_q, a_s, b_q, b_s, c, stream)
+    f = fp8q_gemm_rowscaled_precise if precise else fp8q_gemm_rowscaled
+    f(a_q, a_s, b_q, b_s, c, stream)
     return c
 
 
-def gemm(a_q, a_s, w_q, w_s, out_dtype=None, stream=None):
+def gemm(a_q, a_s, w_q, w_s, out_dtype=None, stream=None, precise=False):
     import torch
     out_dtype = out_dtype or torch.float32
     c = torch.empty((a_q.shape[0], w_q.shape[0]), dtype=out_dtype, device=a_q.device)
-    fp8q_gemm(a_q, a_s, w_q, w_s, c, stream)
+    f = fp8q_gemm_precise if precise else fp8q_gemm
+    f(a_q, a_s, w_q, w_s, c, stream)
     return c
 
 
@@ -255,9 +404,10 @@ def grouped_gemm_fused(x, off, w_q, w_s, mode="f32", out_dtype=None, stream=None
     return c
 
 
-def grouped_gemm(a_q, a_s, off, w_q, w_s, out_dtype=None, stream=None):
+def grouped_gemm(a_q, a_s, off, w_q, w_s, out_dtype=None, stream=None, precise=False):
     import torch
     out_dtype = out_dtype or torch.float32
     c = torch.empty((a_q.shape[0], w_q.shape[1]), dtype=out_dtype, device=a_q.device)
-    fp8q_grouped_gemm(a_q, a_s, off, w_q, w_s, c, stream)
+    f = fp8q_grouped_gemm_precise if precise else fp8q_grouped_gemm
+    f(a_q, a_s, off, w_q, w_s, c, stream)
     return c

@@ -18,10 +18,11 @@ hipError_t launch_quantize_weight(const void* w, int64_t N, int64_t K, uint8_t* 
                                   int mode, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
                        const float* w_s, int64_t M, int64_t N, int64_t K, void* c, int out_bf16,
-                       hipStream_t stream);
+                       int precise, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
                                const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
-                               int64_t N, int64_t K, void* c, int out_bf16, hipStream_t stream);
+                               int64_t N, int64_t K, void* c, int out_bf16, int precise,
+                               hipStream_t stream);
 hipError_t launch_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,
                             void* c, int out_bf16, hipStream_t stream);
 hipError_t launch_quantize_act_t(const void* x, int64_t M, int64_t K, uint8_t* qt, float* st,
@@ -30,7 +31,7 @@ hipError_t launch_quantize_weight_t(const void* w, int64_t N, int64_t K, uint8_t
                                     float* st, int mode, hipStream_t stream);
 hipError_t launch_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
                                  const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
-                                 int out_bf16, hipStream_t stream);
+                                 int out_bf16, int precise, hipStream_t stream);
 hipError_t launch_gemm_cast(const void* x, const uint8_t* w_q, const float* w_s, int64_t M,
                             int64_t N, int64_t K, void* c, int out_bf16, int mode,
                             hipStream_t stream);
@@ -136,9 +137,9 @@ static bool gemm_extent_ok(int64_t rows, int64_t K) {
   return rows <= int64_t(0x7FFFFFFF) / 4 / (K / 128);
 }
 
-fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
-                      const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
-                      fp8q_out_dtype out, hipStream_t stream) {
+static fp8q_status gemm_call(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
+                             const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
+                             fp8q_out_dtype out, int precise, hipStream_t stream) {
   const bool empty_out = (M == 0 || N == 0);
   const bool empty_k = (K == 0);
   if (!empty_out && !c) return FP8Q_ERR_NULL;
@@ -153,13 +154,26 @@ fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
   if (!gemm_extent_ok(M, K)) return FP8Q_ERR_UNSUPPORTED;
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
-  return launched(fp8q::launch_gemm(a_q, a_s, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16, stream));
+  return launched(
+      fp8q::launch_gemm(a_q, a_s, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16, precise, stream));
 }
 
-fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
-                              const int32_t* off, int32_t G, const uint8_t* w_q,
-                              const float* w_s, int64_t N, int64_t K, void* c,
+fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
+                      const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
+                      fp8q_out_dtype out, hipStream_t stream) {
+  return gemm_call(a_q, a_s, w_q, w_s, M, N, K, c, out, 0, stream);
+}
+
+fp8q_status fp8q_gemm_precise(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
+                              const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
                               fp8q_out_dtype out, hipStream_t stream) {
+  return gemm_call(a_q, a_s, w_q, w_s, M, N, K, c, out, 1, stream);
+}
+
+static fp8q_status grouped_call(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                                const int32_t* off, int32_t G, const uint8_t* w_q,
+                                const float* w_s, int64_t N, int64_t K, void* c,
+                                fp8q_out_dtype out, int precise, hipStream_t stream) {
   const bool empty_out = (M_total == 0 || N == 0);
   if (!off) return FP8Q_ERR_NULL;
   if (!empty_out && !c) return FP8Q_ERR_NULL;
@@ -178,7 +192,21 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c,
-                                            out == FP8Q_OUT_BF16, stream));
+                                            out == FP8Q_OUT_BF16, precise, stream));
+}
+
+fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                              const int32_t* off, int32_t G, const uint8_t* w_q,
+                              const float* w_s, int64_t N, int64_t K, void* c,
+                              fp8q_out_dtype out, hipStream_t stream) {
+  return grouped_call(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out, 0, stream);
+}
+
+fp8q_status fp8q_grouped_gemm_precise(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                                      const int32_t* off, int32_t G, const uint8_t* w_q,
+                                      const float* w_s, int64_t N, int64_t K, void* c,
+                                      fp8q_out_dtype out, hipStream_t stream) {
+  return grouped_call(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c, out, 1, stream);
 }
 
 fp8q_status fp8q_quantize_act_t(const void* x_bf16, int64_t M, int64_t K, uint8_t* q_t,
@@ -207,9 +235,9 @@ fp8q_status fp8q_quantize_weight_t(const void* w_bf16, int64_t N, int64_t K, uin
   return launched(fp8q::launch_quantize_weight_t(w_bf16, N, K, q_t, s_t, (int)mode, stream));
 }
 
-fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
-                                const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
-                                fp8q_out_dtype out, hipStream_t stream) {
+static fp8q_status rowscaled_call(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                  const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                  fp8q_out_dtype out, int precise, hipStream_t stream) {
   const bool empty_out = (M == 0 || N == 0);
   if (!empty_out && !c) return FP8Q_ERR_NULL;
   if (!empty_out && K != 0 && (!a_q || !a_s || !b_q || !b_s)) return FP8Q_ERR_NULL;
@@ -224,7 +252,20 @@ fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
   return launched(fp8q::launch_gemm_rowscaled(a_q, a_s, b_q, b_s, M, N, K, c,
-                                              out == FP8Q_OUT_BF16, stream));
+                                              out == FP8Q_OUT_BF16, precise, stream));
+}
+
+fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s, const uint8_t* b_q,
+                                const float* b_s, int64_t M, int64_t N, int64_t K, void* c,
+                                fp8q_out_dtype out, hipStream_t stream) {
+  return rowscaled_call(a_q, a_s, b_q, b_s, M, N, K, c, out, 0, stream);
+}
+
+fp8q_status fp8q_gemm_rowscaled_precise(const uint8_t* a_q, const float* a_s,
+                                        const uint8_t* b_q, const float* b_s, int64_t M,
+                                        int64_t N, int64_t K, void* c, fp8q_out_dtype out,
+                                        hipStream_t stream) {
+  return rowscaled_call(a_q, a_s, b_q, b_s, M, N, K, c, out, 1, stream);
 }
 
 fp8q_status fp8q_gemm_bf16(const void* a, const void* w, int64_t M, int64_t N, int64_t K,

@@ -135,6 +135,21 @@ fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s,
                       void* c, fp8q_out_dtype out, hipStream_t stream);
 
 /*
+ * Precise mode of fp8q_gemm: the same operands, layouts, arguments, errors
+ * and promotion every 128 K, with each chunk partial P_g formed from the E4M3
+ * codes widened exactly to FP16 (every E4M3 value is an FP16 value) by FP16
+ * matrix-core instructions, which accumulate their exact products in FP32
+ * without the FP8 instruction's truncation (the higher-precision accumulation
+ * the why-be.co.kr post 57820 asks for in its hardware-suggestion passage).
+ * Half the matrix-core rate of fp8q_gemm.  Accuracy: see PRECISE ACCURACY
+ * below.
+ */
+fp8q_status fp8q_gemm_precise(const uint8_t* a_q, const float* a_s,
+                              const uint8_t* w_q, const float* w_s,
+                              int64_t M, int64_t N, int64_t K,
+                              void* c, fp8q_out_dtype out, hipStream_t stream);
+
+/*
  * Grouped (per-expert) variant.  Rows [off[e], off[e+1]) of a_q use expert
  * e's weights w_q + e*N*K and scales w_s + e*(N/128)*(K/128).
  *   a_q : [M_total][K] uint8, a_s : [K/128][M_total] float32.
@@ -153,6 +168,14 @@ fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_to
                               const uint8_t* w_q, const float* w_s,
                               int64_t N, int64_t K,
                               void* c, fp8q_out_dtype out, hipStream_t stream);
+
+/* Precise mode of fp8q_grouped_gemm (chunk partials as in fp8q_gemm_precise);
+   everything else as fp8q_grouped_gemm. */
+fp8q_status fp8q_grouped_gemm_precise(const uint8_t* a_q, const float* a_s, int64_t M_total,
+                                      const int32_t* off, int32_t G,
+                                      const uint8_t* w_q, const float* w_s,
+                                      int64_t N, int64_t K,
+                                      void* c, fp8q_out_dtype out, hipStream_t stream);
 
 /*
  * Backward GEMMs (the-good.kr post 2169793, mixed-precision framework
@@ -201,6 +224,13 @@ fp8q_status fp8q_gemm_rowscaled(const uint8_t* a_q, const float* a_s,
                                 const uint8_t* b_q, const float* b_s,
                                 int64_t M, int64_t N, int64_t K,
                                 void* c, fp8q_out_dtype out, hipStream_t stream);
+
+/* Precise mode of fp8q_gemm_rowscaled (chunk partials as in
+   fp8q_gemm_precise); everything else as fp8q_gemm_rowscaled. */
+fp8q_status fp8q_gemm_rowscaled_precise(const uint8_t* a_q, const float* a_s,
+                                        const uint8_t* b_q, const float* b_s,
+                                        int64_t M, int64_t N, int64_t K,
+                                        void* c, fp8q_out_dtype out, hipStream_t stream);
 
 /*
  * BF16 GEMM of the same kernel family, without quantization: the reference

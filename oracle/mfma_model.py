@@ -114,6 +114,50 @@ def gemm_rowscaled(qa, sa, qb, sb):
     return C
 
 
+def truncation_bound(qa, sa, qw, sw, rowscaled=False):
+    """A-priori bound on what steps 1-3 can lose, from the operands alone
+    (float64[M][N]).
+
+    A product p of exponent sum e is an integer multiple of 2^(e - 6) (two
+    E4M3 significands with 3 fraction bits each), so truncation to a multiple
+    of 2^(E - 13) leaves it exact when e >= E - 7, and otherwise changes it by
+    less than min(|p|, 2^(E - 13)).  Summed over the products of every 8-K
+    group and scaled by each chunk's |s_a * s_w|:
+
+        T[m][n] = sum_g |s_a s_w| sum_groups sum_{k: e_k < E - 7} min(|p_k|, 2^(E - 13)).
+
+    |C_model - C_exact| <= T holds by construction; this bound does not use
+    the model's output.  rowscaled: sw is [K/128][N] (1x128 row-group scales
+    of the second operand) instead of [N/128][K/128].
+    """
+    M, K = qa.shape
+    N = qw.shape[0]
+    # |products| are exact in float32 (8 significant bits, 2^-18 .. 2^18)
+    A = np.abs(e4m3.decode(qa)).astype(np.float32)
+    W = np.abs(e4m3.decode(qw)).astype(np.float32)
+    neg = -(1 << 20)
+    exa = np.where(_zero(qa), neg, _EX[qa]).astype(np.int32)
+    exw = np.where(_zero(qw), neg, _EX[qw]).astype(np.int32)
+    out = np.zeros((M, N), dtype=np.float64)
+    for g in range(K // GROUP):
+        ks = slice(g * GROUP, (g + 1) * GROUP)
+        t = (A[:, None, ks] * W[None, :, ks]).reshape(M, N, GROUP // GROUP8, GROUP8)
+        e = (exa[:, None, ks] + exw[None, :, ks]).reshape(M, N, GROUP // GROUP8, GROUP8)
+        E = e.max(axis=3, keepdims=True)
+        lossy = (e > neg // 2) & (e < E - 7)
+        unit = np.ldexp(np.float32(1.0), np.maximum(E, -100) - (KEEP_BITS - 1)).astype(np.float32)
+        # sums of at most 128 terms below 2^18 in float64: exact enough (a bound)
+        lost = np.where(lossy, np.minimum(t, unit), np.float32(0)).sum(axis=(2, 3),
+                                                                    dtype=np.float64)
+        if rowscaled:
+            scale = np.abs(sa[g].astype(np.float64))[:, None] * np.abs(sw[g].astype(np.float64))[None, :]
+        else:
+            col = np.repeat(np.abs(sw[:, g].astype(np.float64)), GROUP)        # [N]
+            scale = np.abs(sa[g].astype(np.float64))[:, None] * col[None, :]
+        out += scale * lost
+    return out
+
+
 def fp32_rounding_bound(qa, sa, qw, sw, abs_bound):
     """Bound on |C_gpu - C_model| from FP32 rounding alone.
 

@@ -1,8 +1,8 @@
 """GPU parity of the backward GEMMs of a linear layer in FP8 (Dgrad and Wgrad)
 through the C ABI: the transposed quantizers bit-exact against the oracle,
-and the GEMM with row-group scales on both operands to the two-tier bar of
-gpu_util.assert_gemm_close (the MFMA model to FP32 rounding; the exact
-oracle to 1e-5 * sum_k |a_k||b_k| where the matrix core's truncation allows).
+and the GEMMs against the exact oracle: the precise calls within 1e-5 *
+sum_k |a_k||b_k| on every checked output (gpu_util.assert_gemm_strict), the
+FP8-MFMA calls within their truncation bound (gpu_util.assert_gemm_bounded).
 
 For Y = X W^T:  dX = dY W   = fp8q_gemm(quantize_act(dY), quantize_weight_t(W))
                 dW = dY^T X = fp8q_gemm_rowscaled(quantize_act_t(dY), quantize_act_t(X))
@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import assert_gemm_close, fq, host, to_dev_bf16
+from gpu_util import assert_gemm_bounded, assert_gemm_strict, fq, host, to_dev_bf16
 from oracle import quant as oquant
 
 pytestmark = pytest.mark.gpu
@@ -71,10 +71,14 @@ def test_gemm_rowscaled_parity(M, N, K):
     qa, sa = f.quantize_act(to_dev_bf16(A))
     qb, sb = f.quantize_act(to_dev_bf16(B))
     c = f.gemm_rowscaled(qa, sa, qb, sb)
+    cp = f.gemm_rowscaled(qa, sa, qb, sb, precise=True)
     torch.cuda.synchronize()
     oa, osa = oquant.quantize_act(A)
     ob, osb = oquant.quantize_act(B)
-    assert_gemm_close(host(c), oa, osa, ob, osb, what=f"rowscaled {M}x{N}x{K}", rowscaled=True)
+    assert_gemm_bounded(host(c), oa, osa, ob, osb, what=f"rowscaled {M}x{N}x{K}",
+                        rowscaled=True)
+    assert_gemm_strict(host(cp), oa, osa, ob, osb, what=f"rowscaled precise {M}x{N}x{K}",
+                       rowscaled=True)
 
 
 def test_gemm_rowscaled_both_tile_widths():
@@ -95,8 +99,8 @@ def test_gemm_rowscaled_both_tile_widths():
         rows = np.sort(np.random.default_rng(M + N).choice(M, 8, replace=False))
         oa, osa = oquant.quantize_act(A[rows])
         ob, osb = oquant.quantize_act(B)
-        assert_gemm_close(host(c)[rows], oa, osa, ob, osb, model_rows=2, rowscaled=True,
-                          what=f"rowscaled {M}x{N}x{K}")
+        assert_gemm_bounded(host(c)[rows], oa, osa, ob, osb, rowscaled=True,
+                            bound_cols=np.arange(0, N, 7), what=f"rowscaled {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
@@ -115,9 +119,11 @@ def test_backward_of_a_linear_layer(out):
     qd, sd = f.quantize_act(dy)
     qwt, swt = f.quantize_weight_t(w)
     dX = f.gemm(qd, sd, qwt, swt, out_dtype=dt)
+    dXp = f.gemm(qd, sd, qwt, swt, out_dtype=dt, precise=True)
     qdt, sdt = f.quantize_act_t(dy)
     qxt, sxt = f.quantize_act_t(x)
     dW = f.gemm_rowscaled(qdt, sdt, qxt, sxt, out_dtype=dt)
+    dWp = f.gemm_rowscaled(qdt, sdt, qxt, sxt, out_dtype=dt, precise=True)
     torch.cuda.synchronize()
     od = oquant.quantize_act(dY)
     owt = oquant.quantize_weight_t(W)
@@ -126,10 +132,13 @@ def test_backward_of_a_linear_layer(out):
     _same(qwt, swt, *owt)
     _same(qdt, sdt, *odt)
     _same(qxt, sxt, *oxt)
-    r1 = assert_gemm_close(dX.float().cpu().numpy(), *od, *owt, out=out, what="dgrad")
-    r2 = assert_gemm_close(dW.float().cpu().numpy(), *odt, *oxt, out=out, what="wgrad",
-                           rowscaled=True)
-    print(f"dgrad {r1}\nwgrad {r2}")
+    r1 = assert_gemm_bounded(dX.float().cpu().numpy(), *od, *owt, out=out, what="dgrad")
+    r2 = assert_gemm_bounded(dW.float().cpu().numpy(), *odt, *oxt, out=out, what="wgrad",
+                             rowscaled=True)
+    r3 = assert_gemm_strict(dXp.float().cpu().numpy(), *od, *owt, out=out, what="dgrad precise")
+    r4 = assert_gemm_strict(dWp.float().cpu().numpy(), *odt, *oxt, out=out,
+                            what="wgrad precise", rowscaled=True)
+    print(f"dgrad {r1}\nwgrad {r2}\ndgrad precise {r3}\nwgrad precise {r4}")
 
 
 def test_wgrad_dense_shape_sampled():
@@ -145,6 +154,7 @@ def test_wgrad_dense_shape_sampled():
     qdt, sdt = f.quantize_act_t(to_dev_bf16(dY))
     qxt, sxt = f.quantize_act_t(to_dev_bf16(X))
     dW = f.gemm_rowscaled(qdt, sdt, qxt, sxt)
+    dWp = f.gemm_rowscaled(qdt, sdt, qxt, sxt, precise=True)
     torch.cuda.synchronize()
     odt = oquant.quantize_act_t(dY)
     oxt = oquant.quantize_act_t(X)
@@ -152,7 +162,9 @@ def test_wgrad_dense_shape_sampled():
     _same(qxt, sxt, *oxt)
     rows = np.sort(np.random.default_rng(23).choice(N, 10, replace=False))
     rows = np.concatenate([[0], rows, [N - 1]])
-    r = assert_gemm_close(host(dW)[rows], odt[0][rows], odt[1][:, rows], *oxt,
-                          what="wgrad dense shape", model_rows=2, rowscaled=True)
-    print(f"wgrad dense shape: {r}")
-    assert r["strict_fraction"] > 0.999
+    r = assert_gemm_bounded(host(dW)[rows], odt[0][rows], odt[1][:, rows], *oxt,
+                            what="wgrad dense shape", rowscaled=True,
+                            bound_cols=np.arange(0, K, 13))
+    rp = assert_gemm_strict(host(dWp)[rows], odt[0][rows], odt[1][:, rows], *oxt,
+                            what="wgrad precise dense shape", rowscaled=True)
+    print(f"wgrad dense shape: fp8 {r}; precise {rp}")

@@ -5,8 +5,9 @@ The fused cast applies fp8q_quantize_act's rule to the same groups and feeds
 the same codes and scales to the same matrix-core sequence, so the bar is
 bitwise equality with quantize-then-GEMM (fp8q_quantize_act followed by
 fp8q_gemm / fp8q_grouped_gemm) on every output, in both scale modes; and,
-directly, the two-tier GEMM bar of gpu_util.assert_gemm_close against the
-oracle on small cases.
+directly, the FP8-MFMA GEMM bar of gpu_util.assert_gemm_bounded (the exact
+oracle within the matrix core's truncation bound plus FP32 rounding) on
+small cases.
 """
 
 import numpy as np
@@ -14,7 +15,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import DEV, assert_gemm_close, fq, host, to_dev_bf16
+from gpu_util import DEV, assert_gemm_bounded, fq, host, to_dev_bf16
 from oracle import quant as oquant
 
 pytestmark = pytest.mark.gpu
@@ -84,8 +85,8 @@ def test_gemm_fused_against_oracle(mode, out):
     qa, sa = oquant.quantize_act(X, mode)
     qw, sw = oquant.quantize_weight(W, mode)
     assert np.array_equal(host(wq), qw)
-    r = assert_gemm_close(c.float().cpu().numpy().astype(np.float64), qa, sa, qw, sw, out=out,
-                          what=f"fused {mode} {out}", model_rows=32)
+    r = assert_gemm_bounded(c.float().cpu().numpy().astype(np.float64), qa, sa, qw, sw,
+                            out=out, what=f"fused {mode} {out}", model_rows=4)
     print(f"fused {mode} {out}: {r}")
 
 
@@ -145,8 +146,8 @@ def test_grouped_fused_all_tile_configs(mode):
         if len(rows) > 24:
             rows = np.sort(np.random.default_rng(e).choice(rows, 24, replace=False))
         qw, sw = oquant.quantize_weight(Wst[e], mode)
-        assert_gemm_close(ch[rows], qa[rows], sa[:, rows], qw, sw, model_rows=4,
-                          what=f"grouped fused {mode} expert {e}")
+        assert_gemm_bounded(ch[rows], qa[rows], sa[:, rows], qw, sw,
+                            what=f"grouped fused {mode} expert {e}")
 
 
 def test_grouped_fused_determinism_and_bf16_out():
