@@ -62,24 +62,84 @@ def parse():
     p.add_argument("--workload", default="dense",
                    choices=["dense", "moe", "decode", "largek", "bf16", "backward", "dense_fused",
                             "decode_fused"])
+    p.add_argument("--precise", action="store_true",
+                   help="the precise GEMM calls (fp8q_gemm_precise, fp8q_grouped_gemm_precise, "
+                        "fp8q_gemm_rowscaled_precise) in place of the FP8-MFMA ones")
     p.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                   help="only run a plain device copy of MIB MiB (3 times): the known-size "
+                   help="only run a streaming device copy of MIB MiB (3 times): the known-size "
                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--stream-ceiling", action="store_true",
+                   help="only time the streaming probe (16 B read, 8 B written per lane: the "
+                        "quantizers' 2:1 traffic) at the quantizers' sizes: their HBM ceiling")
     return p.parse_args()
+
+
+def _probe_lib():
+    import ctypes
+    path = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "libfp8q_probe.so")
+    L = ctypes.CDLL(path)
+    L.fp8q_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_void_p]
+    L.fp8q_probe_stream.restype = ctypes.c_int
+    return L
+
+
+def _probe(L, torch, src, dst, nbytes, ratio):
+    import ctypes
+    st = L.fp8q_probe_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                             nbytes, ratio,
+                             ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"fp8q_probe_stream failed: {st}")
 
 
 def copy_probe(mib):
     import torch
-    n = mib * 1024 * 1024 // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    L = _probe_lib()
+    n = mib * 1024 * 1024
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
     torch.cuda.synchronize()
     for _ in range(3):
-        y.copy_(x)
+        _probe(L, torch, x, y, n, 1)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "launches": 3}))
+    print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 3}))
+
+
+def stream_ceiling(steps):
+    """The streaming probe at each quantizer workload's byte counts (BF16 read,
+    half as many bytes written), timed like the kernels in main(): 4 rotating
+    input sets, `steps` back-to-back launches between HIP events on the launch
+    stream.  GB/s counts read + written bytes."""
+    import torch
+    import workloads
+    L = _probe_lib()
+    W = workloads.WORKLOADS
+    sizes = [("act dense 4096x7168", 4096 * 7168), ("act decode 3980x7168", 3980 * 7168),
+             ("act moe 32768x7168", 32768 * 7168), ("act largek 8192x65536", 8192 * 65536),
+             ("act backward dY 4096x4096", 4096 * 4096)]
+    out = []
+    for name, elems in sizes:
+        nin = 2 * elems
+        sets = 4 if nin < (1 << 30) else 1
+        src = [torch.ones(nin // 4, dtype=torch.float32, device="cuda:0") for _ in range(sets)]
+        dst = [torch.empty(nin // 8, dtype=torch.float32, device="cuda:0") for _ in range(sets)]
+        _probe(L, torch, src[0], dst[0], nin, 2)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            _probe(L, torch, src[i % sets], dst[i % sets], nin, 2)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        moved = nin * 1.5
+        out.append({"case": name, "bytes_read": nin, "bytes_written": nin // 2,
+                    "avg_us": us, "GB_s": moved / us / 1e3, "frac_hbm": moved / us / 1e3 / PEAK_HBM_GBS})
+        del src, dst
+    print(json.dumps({"stream_ceiling": out, "steps": steps, "input_sets": "4 (1 at >= 1 GiB)"}))
 
 
 def gemm_bytes(M, N, K, out_bytes):
@@ -87,7 +147,7 @@ def gemm_bytes(M, N, K, out_bytes):
 
 
 # --------------------------------------------------------------------- setup
-def setup_dense(fq, torch, name, sets, fused=False):
+def setup_dense(fq, torch, name, sets, fused=False, precise=False):
     import workloads
     c = workloads.WORKLOADS[name]
     M, N, K = c["M"], c["N"], c["K"]
@@ -115,11 +175,14 @@ def setup_dense(fq, torch, name, sets, fused=False):
             fq.fp8q_quantize_weight(W, wq, ws)
         elif name == "fp8q_gemm_fused":
             fq.fp8q_gemm_fused(A, wq, ws, C)
+        elif name == "fp8q_gemm_precise":
+            fq.fp8q_gemm_precise(aq, as_, wq, ws, C)
         else:
             fq.fp8q_gemm(aq, as_, wq, ws, C)
 
+    gname = "fp8q_gemm_precise" if precise else "fp8q_gemm"
     order = (["fp8q_quantize_weight", "fp8q_gemm_fused"] if fused else
-             ["fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm"])
+             ["fp8q_quantize_act", "fp8q_quantize_weight", gname])
 
     def step(i):
         for name in order:
@@ -132,9 +195,13 @@ def setup_dense(fq, torch, name, sets, fused=False):
     ]
     if fused:
         kernels.insert(0, ("fp8q_gemm_fused", "mfma", 2.0 * M * N * K, "flop"))
+    if precise:
+        kernels.insert(0, ("fp8q_gemm_precise", "mfma_wide16", 2.0 * M * N * K, "flop"))
     flops = 2.0 * M * N * K
-    tag = name + ("_fused" if fused else "")
+    tag = name + ("_fused" if fused else "") + ("_precise" if precise else "")
     how = "quantized inside the GEMM" if fused else "1x128 act quant"
+    if precise:
+        how += "; precise GEMM (codes widened to FP16, FP16 MFMA)"
     cfg = {"workload": f"{tag}: A {M}x{K} bf16 ({how}), W {N}x{K} bf16 "
                        f"(128x128 block quant), C = A W^T fp32",
            "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
@@ -160,6 +227,19 @@ def setup_bf16(fq, torch, sets):
         C = torch.empty((M, N), dtype=torch.float32, device=dev)
         Cb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         bufs.append((A, W, Wt, aq, as_, wq, ws, C, Cb))
+    # Same-chip context for the FP8 GEMMs: hipBLASLt's FP8 GEMM through
+    # torch._scaled_mm with one scale per tensor (no per-block promotion), on
+    # the codes of the first input set, BF16 out.
+    A, W, Wt, aq, as_, wq, ws, C, Cb = bufs[0]
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    a8 = aq.view(torch.float8_e4m3fn)
+    w8t = wq.view(torch.float8_e4m3fn).t()  # [K][N] column-major view, as _scaled_mm wants
+    try:
+        torch._scaled_mm(a8, w8t, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        have_scaled_mm = True
+    except Exception as e:  # not every build supports it
+        have_scaled_mm = False
+        print(f"torch._scaled_mm unavailable: {e}", file=sys.stderr)
 
     def launch(name, i):
         A, W, Wt, aq, as_, wq, ws, C, Cb = bufs[i % sets]
@@ -167,6 +247,10 @@ def setup_bf16(fq, torch, sets):
             fq.fp8q_gemm_bf16(A, W, C)
         elif name == "fp8q_gemm":
             fq.fp8q_gemm(aq, as_, wq, ws, C)
+        elif name == "fp8q_gemm_precise":
+            fq.fp8q_gemm_precise(aq, as_, wq, ws, C)
+        elif name == "torch_scaled_mm_fp8_per_tensor_hipblaslt":
+            torch._scaled_mm(a8, w8t, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
         else:  # hipBLASLt through torch, BF16 out
             torch.matmul(A, Wt, out=Cb)
 
@@ -178,7 +262,10 @@ def setup_bf16(fq, torch, sets):
         ("fp8q_gemm_bf16", "mfma_bf16", flops, "flop"),
         ("torch_matmul_bf16_hipblaslt", "mfma_bf16", flops, "flop"),
         ("fp8q_gemm", "mfma", flops, "flop"),
+        ("fp8q_gemm_precise", "mfma_wide16", flops, "flop"),
     ]
+    if have_scaled_mm:
+        kernels.append(("torch_scaled_mm_fp8_per_tensor_hipblaslt", "mfma", flops, "flop"))
     cfg = {"workload": f"bf16: A {M}x{K} bf16, W {N}x{K} bf16, C = A W^T fp32 (BF16 GEMM of "
                        f"the FP8 kernel family; the dense workload's inputs)",
            "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
@@ -253,7 +340,7 @@ def setup_backward(fq, torch, sets):
     return step, launch, kernels, 2 * g, cfg
 
 
-def setup_grouped(fq, torch, name, sets, fused=False):
+def setup_grouped(fq, torch, name, sets, fused=False, precise=False):
     import workloads
     c = workloads.WORKLOADS[name]
     dev = "cuda:0"
@@ -298,15 +385,19 @@ def setup_grouped(fq, torch, name, sets, fused=False):
             fq.fp8q_quantize_act(A, aq, as_)
         elif name == "fp8q_grouped_gemm_fused":
             fq.fp8q_grouped_gemm_fused(A, d_off, wq, ws, C)
+        elif name == "fp8q_grouped_gemm_precise":
+            fq.fp8q_grouped_gemm_precise(aq, as_, d_off, wq, ws, C)
         else:
             fq.fp8q_grouped_gemm(aq, as_, d_off, wq, ws, C)
+
+    gname = "fp8q_grouped_gemm_precise" if precise else "fp8q_grouped_gemm"
 
     def step(i):
         if fused:
             launch("fp8q_grouped_gemm_fused", i)
         else:
             launch("fp8q_quantize_act", i)
-            launch("fp8q_grouped_gemm", i)
+            launch(gname, i)
 
     ob = 2 if out_dtype == torch.bfloat16 else 4
     flops = 2.0 * Mt * N * K
@@ -319,7 +410,9 @@ def setup_grouped(fq, torch, name, sets, fused=False):
         # weights and their scales once, the BF16 activations once, the output
         fbytes = G * N * K * (1 + 4 / 16384) + Mt * K * 2 + Mt * N * ob
         kernels.insert(0, ("fp8q_grouped_gemm_fused", "hbm", fbytes, "B"))
-    tag = name + ("_fused" if fused else "")
+    if precise:
+        kernels.insert(0, ("fp8q_grouped_gemm_precise", "hbm", gbytes, "B"))
+    tag = name + ("_fused" if fused else "") + ("_precise" if precise else "")
     how = ("grouped GEMM quantizing its BF16 activations (1x128) inside" if fused else
            "1x128 act quant + grouped GEMM")
     cfg = {"workload": f"{tag}: {G} experts, rows {Mt} (M_e {int(counts.min())}..{int(counts.max())}), "
@@ -368,17 +461,22 @@ def recorded_traffic(kernel, cfg):
 
 
 # --------------------------------------------------------------- cpu baseline
-def cpu_baseline(name):
-    """The oracle, untuned, on a bounded sample of the workload (host cores):
-    the whole dense workload (about 10-20 s), or for the other workloads a
-    row sample whose flops scale the rate."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_sample(name):
+    """(run, flops, what, full_flops): one run of the oracle on a bounded
+    sample of the workload, its flops, a description, the whole workload's
+    flops (the rate is extrapolated to it when they differ)."""
     import workloads
     from oracle import gemm as ogemm, quant as oquant
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     if name == "backward":
         c = workloads.WORKLOADS["dense"]
         M, N, K = c["M"], c["N"], c["K"]
@@ -386,52 +484,91 @@ def cpu_baseline(name):
         X, _ = workloads.dense_inputs("dense", rows_w=np.arange(128))
         dY = workloads.bf16_bits(
             (np.random.default_rng(c["seed"] + 7).standard_normal((M, N)) * 1e-2).astype(np.float32))
-        t0 = time.perf_counter()
-        qdt, sdt = oquant.quantize_act_t(dY)
-        qxt, sxt = oquant.quantize_act_t(X)
-        ogemm.gemm_rowscaled(qdt[:rows], sdt[:, :rows], qxt, sxt)
-        dt = time.perf_counter() - t0
-        flops = 2.0 * rows * K * M
-        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-                "sample": f"Wgrad rows 0..{rows - 1} of dW: oracle quantize_act_t of dY ({M}x{N}) "
-                          f"and X ({M}x{K}) + exact row-scaled GEMM {rows}x{K}x{M}; {dt:.1f} s wall; "
-                          f"value = 2*{rows}*{K}*{M} / wall"}
+
+        def run():
+            qdt, sdt = oquant.quantize_act_t(dY)
+            qxt, sxt = oquant.quantize_act_t(X)
+            ogemm.gemm_rowscaled(qdt[:rows], sdt[:, :rows], qxt, sxt)
+        return (run, 2.0 * rows * K * M,
+                f"Wgrad rows 0..{rows - 1} of dW: oracle quantize_act_t of dY ({M}x{N}) and X "
+                f"({M}x{K}) + exact row-scaled GEMM {rows}x{K}x{M}", 2.0 * 2 * M * N * K)
     if name == "bf16":
         c = workloads.WORKLOADS["dense"]
-        M, N, K = c["M"], c["N"], c["K"]
-        A, W = workloads.dense_inputs("dense")
-        t0 = time.perf_counter()
-        ogemm.gemm_bf16(A, W)
-        dt = time.perf_counter() - t0
-        return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-                "kind": "oracle",
-                "sample": f"the whole bf16 workload: oracle gemm_bf16 (float64 matmul of "
-                          f"the BF16 values) {M}x{N}x{K}; {dt:.1f} s wall; "
-                          f"value = 2*M*N*K / wall"}
+        M, N, K = 1024, 1024, c["K"]
+        A, W = workloads.dense_inputs("dense", rows_a=np.arange(M), rows_w=np.arange(N))
+        return (lambda: ogemm.gemm_bf16(A, W), 2.0 * M * N * K,
+                f"rows 0..{M - 1} of A and 0..{N - 1} of W: oracle gemm_bf16 (float64 matmul "
+                f"of the BF16 values) {M}x{N}x{K}", 2.0 * c["M"] * c["N"] * K)
     c = workloads.WORKLOADS[name]
-    if name == "dense":
-        M, N, K = c["M"], c["N"], c["K"]
-        A, W = workloads.dense_inputs(name)
-        what = "the whole dense workload"
-    elif name == "largek":
-        M, N, K = 64, 512, c["K"]
+    if name in ("dense", "largek"):
+        M, N = (2048, 2048) if name == "dense" else (64, 512)
+        K = c["K"]
         A, W = workloads.dense_inputs(name, rows_a=np.arange(M), rows_w=np.arange(N))
         what = f"rows 0..{M - 1} of A and 0..{N - 1} of W"
+        full = 2.0 * c["M"] * c["N"] * K
     else:
         M, N, K = 256, c["N"], c["K"]
         outl = workloads.outlier_channels(K, c["seed"], c["outlier_frac"], c["outlier_count"])
         A = workloads.act_rows(np.arange(M), K, c["seed"], c["act_std"], outl, c["outlier_mult"])
         W = workloads.weight_rows(np.arange(N), K, c["seed"], c["w_std"])
         what = f"{M} activation rows x one expert's {N}x{K} weight"
-    t0 = time.perf_counter()
-    qa, sa = oquant.quantize_act(A)
-    qw, sw = oquant.quantize_weight(W)
-    ogemm.gemm(qa, sa, qw, sw)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * M * N * K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{what}: oracle quantize_act({M}x{K}) + quantize_weight({N}x{K}) + exact "
-                      f"float64 per-chunk GEMM {M}x{N}x{K}; {dt:.1f} s wall; value = 2*M*N*K / wall"}
+        if name == "moe":
+            full = 2.0 * c["tokens"] * c["topk"] * N * K
+        else:
+            counts, _ = workloads.decode_counts(c["experts"], c["m_lo"], c["m_hi"], c["seed"])
+            full = 2.0 * float(counts.sum()) * N * K
+
+    def run():
+        qa, sa = oquant.quantize_act(A)
+        qw, sw = oquant.quantize_weight(W)
+        ogemm.gemm(qa, sa, qw, sw)
+    return (run, 2.0 * M * N * K,
+            f"{what}: oracle quantize_act({M}x{K}) + quantize_weight({N}x{K}) + exact float64 "
+            f"per-chunk GEMM {M}x{N}x{K}", full)
+
+
+def cpu_baseline(name):
+    """The oracle, untuned, on the host: a bounded sample of the workload run
+    3 times with every BLAS thread the process may use and 3 times on one
+    thread; wall clock of each run (input generation excluded), median
+    reported.  value = sample flops / median wall (TFLOP/s), extrapolated to
+    the whole workload when the sample is a slice."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threadpool_limits = None
+        blas = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    run, flops, what, full = _cpu_sample(name)
+
+    def median_wall(reps=3):
+        walls = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            run()
+            walls.append(time.perf_counter() - t0)
+        return float(np.median(walls)), walls
+
+    wall_all, walls_all = median_wall()
+    wall_one, walls_one = None, []
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            wall_one, walls_one = median_wall()
+    sliced = abs(full - flops) > 1e-6 * full
+    rec = {"value": flops / wall_all / 1e12, "unit": "TFLOP/s", "cores": int(blas),
+           "kind": "oracle",
+           "sample": f"{what}; median of 3 runs {', '.join(f'{w:.2f}' for w in walls_all)} s; "
+                     f"value = sample flops / median wall"
+                     + ("; extrapolated: the rate is taken to hold for the whole workload"
+                        if sliced else "; the whole workload"),
+           "value_1core": (flops / wall_one / 1e12) if wall_one else None,
+           "walls_1core_s": walls_one,
+           "extrapolated": bool(sliced),
+           "workload_time_s": full / (flops / wall_all) if sliced else wall_all,
+           "cpu_model": _cpu_model(), "usable_cpus": int(usable or 1),
+           "blas_threads": int(blas)}
+    return rec
 
 
 # ----------------------------------------------------------------------- main
@@ -444,6 +581,9 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    if args.stream_ceiling:
+        stream_ceiling(args.steps)
+        return
     import torch
     import fine_grained_block_fp8q_amd as fq
 
@@ -452,13 +592,14 @@ def main():
     base = args.workload.replace("_fused", "")
     fused = base != args.workload
     if base in ("dense", "largek"):
-        step, launch, kernels, flops, cfg = setup_dense(fq, torch, base, sets, fused)
+        step, launch, kernels, flops, cfg = setup_dense(fq, torch, base, sets, fused, args.precise)
     elif args.workload == "bf16":
         step, launch, kernels, flops, cfg = setup_bf16(fq, torch, sets)
     elif args.workload == "backward":
         step, launch, kernels, flops, cfg = setup_backward(fq, torch, sets)
     else:
-        step, launch, kernels, flops, cfg = setup_grouped(fq, torch, base, sets, fused)
+        step, launch, kernels, flops, cfg = setup_grouped(fq, torch, base, sets, fused,
+                                                          args.precise)
     torch.cuda.synchronize()
 
     # Timed region: exactly `steps` steps, synchronized on both sides.
@@ -506,6 +647,7 @@ def main():
         else:
             ach = work / (avg_ms * 1e-3) / 1e12
             peak_key, peak = (("frac_bf16_peak", PEAK_BF16_TFLOPS) if bound == "mfma_bf16"
+                              else ("frac_fp16_peak", PEAK_BF16_TFLOPS) if bound == "mfma_wide16"
                               else ("frac_fp8_peak", PEAK_FP8_TFLOPS))
             kout[kname] = {"avg_us": avg_ms * 1e3, "TFLOP_s": ach, peak_key: ach / peak,
                            "flops": work, **spread}
@@ -546,6 +688,22 @@ def main():
                     "fused": dom["avg_us"],
                     "quantize_act_plus_grouped_gemm": (kout["fp8q_quantize_act"]["avg_us"]
                                                        + kout["fp8q_grouped_gemm"]["avg_us"])}}
+    elif args.precise and args.workload in ("dense", "largek"):
+        dom = kout["fp8q_gemm_precise"]
+        roof = {"kernel": "fp8q_gemm_precise", "bound": "mfma", "achieved": dom["TFLOP_s"],
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dom["TFLOP_s"] / PEAK_BF16_TFLOPS,
+                "frac_of_fp8_peak": dom["TFLOP_s"] / PEAK_FP8_TFLOPS,
+                "peak_note": "FP16 MFMA dense peak (the instruction the precise mode runs); "
+                             "frac_of_fp8_peak against the FP8 dense peak",
+                "traffic": recorded_traffic("fp8q_gemm_precise", cfg)}
+    elif args.precise:
+        dom = kout["fp8q_grouped_gemm_precise"]
+        dom["TFLOP_s"] = flops / (dom["avg_us"] * 1e-6) / 1e12
+        dom["frac_fp8_peak"] = dom["TFLOP_s"] / PEAK_FP8_TFLOPS
+        dom["frac_fp16_peak"] = dom["TFLOP_s"] / PEAK_BF16_TFLOPS
+        roof = {"kernel": "fp8q_grouped_gemm_precise", "bound": "hbm", "achieved": dom["GB_s"],
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom["GB_s"] / PEAK_HBM_GBS,
+                "traffic": recorded_traffic("fp8q_grouped_gemm_precise", cfg)}
     elif args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm"]
         traffic = recorded_traffic("fp8q_gemm", cfg)

@@ -67,9 +67,12 @@ lib.fp8q_status_string.argtypes = [_st]
 lib.fp8q_status_string.restype = ctypes.c_char_p
 lib.fp8q_abi_version.argtypes = []
 lib.fp8q_abi_version.restype = ctypes.c_int
+lib.fp8q_debug_checks.argtypes = []
+lib.fp8q_debug_checks.restype = ctypes.c_int
 
 # enums (include/fp8q.h)
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ENUM, ERR_DEVICE, ERR_LAUNCH, ERR_UNSUPPORTED = range(8)
+(OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ENUM, ERR_DEVICE, ERR_LAUNCH, ERR_UNSUPPORTED,
+ ERR_OFFSETS) = range(9)
 SCALE_F32, SCALE_POW2 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 GROUP = 128

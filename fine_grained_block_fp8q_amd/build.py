@@ -15,6 +15,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8q.so")
+# The same sources with FP8Q_DEBUG_CHECKS: grouped calls synchronize after the
+# launch and report invalid device offsets as FP8Q_ERR_OFFSETS.
+LIB_DEBUG = os.path.join(PKG, "libfp8q_debug.so")
+# Measurement support for bench.py --copy-probe (streaming-bandwidth ceiling
+# and counter calibration); not part of the method's C ABI.
+LIB_PROBE = os.path.join(PKG, "libfp8q_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -51,21 +57,40 @@ def _run(cmd):
     return out
 
 
-def build(verbose=False):
-    """Compile every HIP source for gfx950 and link libfp8q.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _build_one(lib, tag, defines, verbose):
     objs = []
     for src, extra in SOURCES.items():
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(BUILD_DIR, src.replace(".hip", f"{tag}.o"))
+        cmd = [HIPCC, *COMMON, *defines, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         out = _run(cmd)
         if verbose and out.strip():
             print(out)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every HIP source for gfx950 and link libfp8q.so and its
+    FP8Q_DEBUG_CHECKS variant libfp8q_debug.so (always rebuilds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(3) as ex:
+        jobs = [ex.submit(_build_one, LIB, "", [], verbose),
+                ex.submit(_build_one, LIB_DEBUG, "_debug", ["-DFP8Q_DEBUG_CHECKS"], verbose),
+                ex.submit(_build_probe, verbose)]
+        for j in jobs:
+            j.result()
     return LIB
+
+
+def _build_probe(verbose):
+    tmp = LIB_PROBE + ".tmp"
+    out = _run([HIPCC, *COMMON, "-shared", os.path.join(CSRC, "stream_probe.hip"), "-o", tmp])
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIB_PROBE)
 
 
 if __name__ == "__main__":

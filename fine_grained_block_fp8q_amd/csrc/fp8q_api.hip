@@ -38,6 +38,9 @@ hipError_t launch_gemm_cast(const void* x, const uint8_t* w_q, const float* w_s,
 hipError_t launch_grouped_gemm_cast(const void* x, int64_t M_total, const int32_t* off, int G,
                                     const uint8_t* w_q, const float* w_s, int64_t N, int64_t K,
                                     void* c, int out_bf16, int mode, hipStream_t stream);
+#ifdef FP8Q_DEBUG_CHECKS
+hipError_t offsets_error_take(hipStream_t stream, int* flag);
+#endif
 }  // namespace fp8q
 
 namespace {
@@ -76,6 +79,22 @@ fp8q_status launched(hipError_t e) {
   return FP8Q_ERR_LAUNCH;
 }
 
+// A grouped launch's status.  Debug builds (FP8Q_DEBUG_CHECKS) synchronize
+// the stream and report the kernel's verdict on the device offsets.
+fp8q_status grouped_launched(hipError_t e, hipStream_t stream) {
+  const fp8q_status st = launched(e);
+#ifdef FP8Q_DEBUG_CHECKS
+  if (st == FP8Q_OK) {
+    int flag = 0;
+    if (fp8q::offsets_error_take(stream, &flag) != hipSuccess) return launched(hipErrorUnknown);
+    if (flag) return FP8Q_ERR_OFFSETS;
+  }
+#else
+  (void)stream;
+#endif
+  return st;
+}
+
 bool valid_mode(int m) { return m == FP8Q_SCALE_F32 || m == FP8Q_SCALE_POW2; }
 bool valid_out(int o) { return o == FP8Q_OUT_F32 || o == FP8Q_OUT_BF16; }
 
@@ -84,6 +103,14 @@ bool valid_out(int o) { return o == FP8Q_OUT_F32 || o == FP8Q_OUT_BF16; }
 extern "C" {
 
 int fp8q_abi_version(void) { return FP8Q_ABI_VERSION; }
+
+int fp8q_debug_checks(void) {
+#ifdef FP8Q_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
 
 const char* fp8q_status_string(fp8q_status st) {
   switch (st) {
@@ -98,6 +125,9 @@ const char* fp8q_status_string(fp8q_status st) {
     case FP8Q_ERR_DEVICE: return "FP8Q_ERR_DEVICE: no current HIP device, or it is not gfx950";
     case FP8Q_ERR_LAUNCH: return "FP8Q_ERR_LAUNCH: kernel launch failed";
     case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: not implemented in this build";
+    case FP8Q_ERR_OFFSETS:
+      return "FP8Q_ERR_OFFSETS: device offsets not 0 = off[0] <= ... <= off[G] <= M_total "
+             "(reported by FP8Q_DEBUG_CHECKS builds)";
   }
   return "FP8Q_ERR_UNKNOWN: not a status code";
 }
@@ -191,8 +221,9 @@ static fp8q_status grouped_call(const uint8_t* a_q, const float* a_s, int64_t M_
   if (!gemm_extent_ok(M_total, K)) return FP8Q_ERR_UNSUPPORTED;
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
-  return launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K, c,
-                                            out == FP8Q_OUT_BF16, precise, stream));
+  return grouped_launched(fp8q::launch_grouped_gemm(a_q, a_s, M_total, off, G, w_q, w_s, N, K,
+                                                    c, out == FP8Q_OUT_BF16, precise, stream),
+                          stream);
 }
 
 fp8q_status fp8q_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
@@ -326,8 +357,10 @@ fp8q_status fp8q_grouped_gemm_fused(const void* x_bf16, int64_t M_total, const i
   if (K > (int64_t(1) << 21)) return FP8Q_ERR_UNSUPPORTED;
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
-  return launched(fp8q::launch_grouped_gemm_cast(x_bf16, M_total, off, G, w_q, w_s, N, K, c,
-                                                 out == FP8Q_OUT_BF16, (int)mode, stream));
+  return grouped_launched(fp8q::launch_grouped_gemm_cast(x_bf16, M_total, off, G, w_q, w_s, N,
+                                                         K, c, out == FP8Q_OUT_BF16, (int)mode,
+                                                         stream),
+                          stream);
 }
 
 }  // extern "C"

@@ -879,6 +879,23 @@ __device__ __forceinline__ int snake_position(int r, int G) {
 }
 
 __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+#ifdef FP8Q_DEBUG_CHECKS
+// Set by a grouped launch that found invalid offsets (debug builds): read and
+// cleared by the host entry points after their synchronization.
+__device__ int g_offsets_error = 0;
+
+hipError_t offsets_error_take(hipStream_t stream, int* flag) {
+  const int zero = 0;
+  hipError_t e = hipMemcpyFromSymbolAsync(flag, HIP_SYMBOL(g_offsets_error), sizeof(int), 0,
+                                          hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && *flag)
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_offsets_error), &zero, sizeof(int), 0,
+                          hipMemcpyHostToDevice);
+  return e;
+}
+#endif
 constexpr int kMaxExpertsLds = 1024;
 constexpr int kGroupedThreads = 512;
 constexpr int kGroupedLds =
@@ -913,8 +930,23 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_gemm_kernel(
   // a tile leave before any LDS work.
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // The same pass validates the offsets (0 = off[0] <= ... <= off[G] <=
+  // M_total): every wave of every workgroup reads the same values and comes
+  // to the same verdict, and with invalid offsets the whole launch returns
+  // here, before any load or store.
   int sum_mt = 0;
-  for (int e = lane; e < G; e += 64) sum_mt += mtiles(off[e + 1] - off[e]);
+  bool bad = lane == 0 && (off[0] != 0 || (int64_t)off[G] > M_total);
+  for (int e = lane; e < G; e += 64) {
+    const int lo = off[e], hi = off[e + 1];
+    bad = bad || hi < lo;
+    sum_mt += mtiles(hi - lo);
+  }
+  if (__ballot(bad) != 0) {
+#ifdef FP8Q_DEBUG_CHECKS
+    if (blockIdx.x == 0 && tid == 0) g_offsets_error = 1;
+#endif
+    return;
+  }
   for (int d = 32; d >= 1; d >>= 1) sum_mt += __shfl_xor(sum_mt, d);
   // (equal in every lane; readfirstlane keeps everything derived from it scalar)
   const int total = __builtin_amdgcn_readfirstlane(sum_mt) * tiles_n;  // real tiles

@@ -11,8 +11,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8q.h")
 LIB = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "libfp8q.so")
+LIB_DEBUG = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "libfp8q_debug.so")
 
-OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_DEVICE, E_LAUNCH, E_UNSUP = range(8)
+OK, E_NULL, E_SHAPE, E_ALIGN, E_ENUM, E_DEVICE, E_LAUNCH, E_UNSUP, E_OFFSETS = range(9)
 
 
 def _declared_functions():
@@ -21,16 +22,18 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(fp8q_[a-z0-9_]+)\s*\(", text)))
 
 
-@pytest.fixture(scope="module")
-def lib():
-    if not os.path.exists(LIB):
-        pytest.fail("libfp8q.so is not built (python fine_grained_block_fp8q_amd/build.py)")
-    L = ctypes.CDLL(LIB)
+def _load(path):
+    if not os.path.exists(path):
+        pytest.fail(f"{os.path.basename(path)} is not built (python fine_grained_block_fp8q_amd/build.py)")
+    L = ctypes.CDLL(path)
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.fp8q_quantize_act.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_quantize_weight.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
+    L.fp8q_gemm_precise.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_grouped_gemm.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
+    L.fp8q_grouped_gemm_precise.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
+    L.fp8q_gemm_rowscaled_precise.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_gemm_bf16.argtypes = [p, p, i64, i64, i64, p, i32, p]
     L.fp8q_quantize_act_t.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_quantize_weight_t.argtypes = [p, i64, i64, p, p, i32, p]
@@ -40,6 +43,13 @@ def lib():
     L.fp8q_status_string.restype = ctypes.c_char_p
     L.fp8q_status_string.argtypes = [ctypes.c_int]
     return L
+
+
+@pytest.fixture(scope="module", params=["release", "debug_checks"])
+def lib(request):
+    """Both builds: the library and its FP8Q_DEBUG_CHECKS variant validate
+    arguments on the host identically."""
+    return _load(LIB if request.param == "release" else LIB_DEBUG)
 
 
 def _no_device():
@@ -52,17 +62,19 @@ def _no_device():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm",
-                          "fp8q_grouped_gemm", "fp8q_gemm_bf16", "fp8q_quantize_act_t",
-                          "fp8q_quantize_weight_t", "fp8q_gemm_rowscaled", "fp8q_gemm_fused",
-                          "fp8q_grouped_gemm_fused", "fp8q_status_string",
-                          "fp8q_abi_version"}
+                          "fp8q_gemm_precise", "fp8q_grouped_gemm", "fp8q_grouped_gemm_precise",
+                          "fp8q_gemm_bf16", "fp8q_quantize_act_t", "fp8q_quantize_weight_t",
+                          "fp8q_gemm_rowscaled", "fp8q_gemm_rowscaled_precise", "fp8q_gemm_fused",
+                          "fp8q_grouped_gemm_fused", "fp8q_status_string", "fp8q_abi_version",
+                          "fp8q_debug_checks"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8q_abi_version() == 1
-    for s in range(8):
+    assert lib.fp8q_abi_version() == 2
+    assert lib.fp8q_debug_checks() in (0, 1)
+    for s in range(9):
         txt = lib.fp8q_status_string(s).decode()
         assert txt.startswith("FP8Q_")
     assert "UNKNOWN" in lib.fp8q_status_string(99).decode()
@@ -97,8 +109,14 @@ def test_quantize_weight_validation(lib):
     assert f(None, 0, 0, None, None, 0, None) == OK
 
 
-def test_gemm_validation(lib):
-    f = lib.fp8q_gemm
+def test_debug_checks_flag():
+    assert _load(LIB).fp8q_debug_checks() == 0
+    assert _load(LIB_DEBUG).fp8q_debug_checks() == 1
+
+
+@pytest.mark.parametrize("name", ["fp8q_gemm", "fp8q_gemm_precise"])
+def test_gemm_validation(lib, name):
+    f = getattr(lib, name)
     assert f(A, A, A, A, 4, 128, 128, None, 0, None) == E_NULL
     assert f(None, A, A, A, 4, 128, 128, A, 0, None) == E_NULL
     assert f(A, None, A, A, 4, 128, 128, A, 0, None) == E_NULL
@@ -116,8 +134,9 @@ def test_gemm_validation(lib):
     assert f(A, A, A, A, 1 << 29, 128, 128, A, 0, None) == E_UNSUP    # scale offsets >= 2^31
 
 
-def test_grouped_gemm_validation(lib):
-    f = lib.fp8q_grouped_gemm
+@pytest.mark.parametrize("name", ["fp8q_grouped_gemm", "fp8q_grouped_gemm_precise"])
+def test_grouped_gemm_validation(lib, name):
+    f = getattr(lib, name)
     assert f(A, A, 8, None, 2, A, A, 128, 128, A, 0, None) == E_NULL
     assert f(A, A, 8, A, 2, A, A, 128, 128, None, 0, None) == E_NULL
     assert f(A, A, 8, A, 0, A, A, 128, 128, A, 0, None) == E_SHAPE
@@ -163,8 +182,9 @@ def test_transposed_quantizer_validation(lib):
         assert f(A, 128, 128, A, A, 2, None) == E_ENUM
 
 
-def test_gemm_rowscaled_validation(lib):
-    f = lib.fp8q_gemm_rowscaled
+@pytest.mark.parametrize("name", ["fp8q_gemm_rowscaled", "fp8q_gemm_rowscaled_precise"])
+def test_gemm_rowscaled_validation(lib, name):
+    f = getattr(lib, name)
     assert f(A, A, A, A, 4, 128, 128, None, 0, None) == E_NULL
     assert f(A, A, None, A, 4, 128, 128, A, 0, None) == E_NULL
     assert f(A, A, A, None, 4, 128, 128, A, 0, None) == E_NULL
@@ -229,3 +249,6 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert lib.fp8q_gemm_rowscaled(A, A, A, A, 4, 128, 128, A, 0, None) == E_DEVICE
     assert lib.fp8q_gemm_fused(A, A, A, 4, 128, 128, A, 0, 1, None) == E_DEVICE
     assert lib.fp8q_grouped_gemm_fused(A, 8, A, 2, A, A, 128, 128, A, 0, 0, None) == E_DEVICE
+    assert lib.fp8q_gemm_precise(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
+    assert lib.fp8q_grouped_gemm_precise(A, A, 8, A, 2, A, A, 128, 128, A, 0, None) == E_DEVICE
+    assert lib.fp8q_gemm_rowscaled_precise(A, A, A, A, 4, 128, 128, A, 0, None) == E_DEVICE

@@ -185,3 +185,31 @@ def test_weight_dense_full_size_sampled_blocks():
         rows = slice(nb * 128, (nb + 1) * 128)
         rq, rs = oquant.quantize_weight(W[rows], "f32")
         _assert_same(gq[rows], gs[nb:nb + 1], rq, rs, f"weight dense block row {nb}")
+
+
+def test_act_cast_sweep_every_bf16_against_128_group_maxima():
+    """The hardware FP32 -> E4M3 conversion inside fp8q_quantize_act against
+    oracle.e4m3.encode on a dense sweep of its inputs fl32(x * fl32(448 / a)):
+    every finite BF16 x with |x| <= a (both signs, subnormals included)
+    against each of the 128 BF16 group maxima a in [1, 2) (every BF16
+    mantissa, so inv takes 128 different significands).  The sweep puts
+    thousands of inputs within one FP32 ulp of E4M3 rounding midpoints (ties
+    and their neighbours), in the normal and the subnormal E4M3 range."""
+    maxima = np.arange(0x3F80, 0x4000, dtype=np.uint16)
+    blocks = [_exhaustive_bf16_rows(int(a)) for a in maxima]
+    bits = np.concatenate(blocks, axis=0)
+    gq, gs = _gpu_act(bits, "f32")
+    rq, rs = oquant.quantize_act(bits, "f32")
+    _assert_same(gq, gs, rq, rs, "act cast sweep over 128 group maxima")
+    # coverage: inputs of the cast within one FP32 ulp of an E4M3 midpoint
+    from oracle import e4m3
+    x = oquant.bf16_bits_to_f32(bits).reshape(bits.shape[0], -1, 128)
+    inv = np.float32(448.0) / np.abs(x[:, :, :1])
+    v = np.abs((x * inv).astype(np.float32)).ravel()
+    pos = np.sort(e4m3.DECODE_TABLE[:0x7F].astype(np.float64))
+    mids = (pos[1:] + pos[:-1]) / 2
+    j = np.clip(np.searchsorted(mids, v), 1, len(mids) - 1)
+    d = np.minimum(np.abs(v - mids[j]), np.abs(v - mids[j - 1]))
+    near = int(np.sum(d <= np.spacing(v.astype(np.float32)).astype(np.float64)))
+    print(f"cast sweep: {v.size} inputs, {near} within one FP32 ulp of a midpoint")
+    assert near > 1000

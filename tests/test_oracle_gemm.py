@@ -224,3 +224,49 @@ def test_backward_gemms_of_a_linear_layer():
     assert np.linalg.norm(dW - refw) / np.linalg.norm(refw) < 0.06
     # a transposed operand would be far off
     assert np.linalg.norm(dW.T[:N, :N] - refw[:N, :N]) / np.linalg.norm(refw[:N, :N]) > 0.5
+
+
+def test_abs_bound_exact_rational_bruteforce():
+    """abs_bound (the tolerance's sum_k |dec(a_k) s_a| |dec(w_k) s_w|) against a
+    Fraction triple loop over the DECODED values: signed codes (the bound must
+    take magnitudes), a flushed group (scale 0), subnormal codes, a negative
+    scale (magnitude taken), and two weight blocks with different scales (a
+    transposed or misindexed scale table fails)."""
+    rng = np.random.default_rng(12)
+    M, N, K = 5, 256, 384
+    qa = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    qw = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    qa[(qa & 0x7F) == 0x7F] = 0x01      # no NaN codes; 0x01 is the smallest subnormal
+    qw[(qw & 0x7F) == 0x7F] = 0x81
+    sa = rng.uniform(0.5, 2.0, size=(K // 128, M)).astype(np.float32)
+    sw = rng.uniform(0.5, 2.0, size=(N // 128, K // 128)).astype(np.float32)
+    sa[1, 2] = 0.0                        # a flushed group
+    sw[1, 0] = -sw[1, 0]                  # a sign the bound must drop
+    got = gemm.abs_bound(qa, sa, qw, sw)
+    dec = [Fraction(float(v)) if np.isfinite(v) else None for v in e4m3.DECODE_TABLE]
+    for m in range(M):
+        for n in (0, 5, 127, 128, 200, 255):
+            want = Fraction(0)
+            for k in range(K):
+                g = k // 128
+                want += (abs(dec[qa[m, k]] * Fraction(float(sa[g, m])))
+                         * abs(dec[qw[n, k]] * Fraction(float(sw[n // 128, g]))))
+            # float64 accumulation over 3 chunks: within 4 * 2^-53 relative
+            assert abs(Fraction(float(got[m, n])) - want) <= want * Fraction(4, 2**53), (m, n)
+    assert np.all(got >= np.abs(gemm.gemm(qa, sa, qw, sw)))
+
+
+def test_abs_bound_rowscaled_exact_rational_bruteforce():
+    rng = np.random.default_rng(13)
+    M, N, K = 4, 128, 256
+    qa = rng.integers(0, 127, size=(M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)) << 7).astype(np.uint8)
+    qb = rng.integers(0, 127, size=(N, K)).astype(np.uint8)
+    sa = rng.uniform(0.5, 2.0, size=(K // 128, M)).astype(np.float32)
+    sb = rng.uniform(0.5, 2.0, size=(K // 128, N)).astype(np.float32)
+    got = gemm.abs_bound_rowscaled(qa, sa, qb, sb)
+    dec = [Fraction(float(v)) if np.isfinite(v) else None for v in e4m3.DECODE_TABLE]
+    for m in range(M):
+        for n in (0, 3, 64, 127):
+            want = sum(abs(dec[qa[m, k]] * Fraction(float(sa[k // 128, m])))
+                       * abs(dec[qb[n, k]] * Fraction(float(sb[k // 128, n]))) for k in range(K))
+            assert abs(Fraction(float(got[m, n])) - want) <= want * Fraction(4, 2**53), (m, n)
