@@ -19,6 +19,7 @@ then call the entry points.
 
 import ctypes
 import os
+import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp8q.so")
@@ -92,6 +93,47 @@ def _check(status, where):
         raise Fp8qError(status, where)
 
 
+class _Bound(Exception):
+    """Raised inside a wrapper called through bind(): carries the C call."""
+
+    def __init__(self, call):
+        super().__init__("bound call")
+        self.call = call
+
+
+_capture = threading.local()
+
+
+def _invoke(cfunc, args, where):
+    if getattr(_capture, "on", False):
+        raise _Bound((cfunc, args, where))
+    _check(cfunc(*args), where)
+
+
+def bind(fn, *args, **kwargs):
+    """Validate a call once and return a zero-argument callable that repeats
+    it: the same C entry point with the same pointers, sizes and stream, and
+    none of the per-call host checks (for launch loops whose kernels are
+    shorter than those checks).  The tensors must stay alive and keep their
+    storage while the callable is used; a non-OK status still raises.
+    Example: run = bind(fp8q_quantize_act, x, q, s); run(); run()."""
+    _capture.on = True
+    try:
+        fn(*args, **kwargs)
+    except _Bound as b:
+        cfunc, cargs, where = b.call
+    else:
+        raise TypeError(f"{getattr(fn, '__name__', fn)} is not an entry-point wrapper")
+    finally:
+        _capture.on = False
+
+    def run():
+        st = cfunc(*cargs)
+        if st != OK:
+            raise Fp8qError(st, where)
+    return run
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -160,7 +202,7 @@ def fp8q_quantize_act(x, q, s, mode="f32", stream=None):
     _req(w, "x", x, ["bf16"], (M, K), x.device)
     _req(w, "q", q, ["u8"], (M, K), x.device)
     _req(w, "s", s, ["f32"], (K // GROUP, M), x.device)
-    _check(lib.fp8q_quantize_act(_ptr(x), M, K, _ptr(q), _ptr(s), _MODES[mode],
+    _invoke(lib.fp8q_quantize_act, (_ptr(x), M, K, _ptr(q), _ptr(s), _MODES[mode],
                                  _stream(stream, x.device)), "fp8q_quantize_act")
 
 
@@ -172,7 +214,7 @@ def fp8q_quantize_weight(w, q, s, mode="f32", stream=None):
     _req(wh, "w", w, ["bf16"], (N, K), w.device)
     _req(wh, "q", q, ["u8"], (N, K), w.device)
     _req(wh, "s", s, ["f32"], (N // GROUP, K // GROUP), w.device)
-    _check(lib.fp8q_quantize_weight(_ptr(w), N, K, _ptr(q), _ptr(s), _MODES[mode],
+    _invoke(lib.fp8q_quantize_weight, (_ptr(w), N, K, _ptr(q), _ptr(s), _MODES[mode],
                                     _stream(stream, w.device)), "fp8q_quantize_weight")
 
 
@@ -192,14 +234,14 @@ def _gemm_args(where, a_q, a_s, w_q, w_s, c):
 def fp8q_gemm(a_q, a_s, w_q, w_s, c, stream=None):
     """c[M][N] (float32 or bfloat16) = block-scaled a_q[M][K] x w_q[N][K]^T."""
     M, N, K, out = _gemm_args("fp8q_gemm", a_q, a_s, w_q, w_s, c)
-    _check(lib.fp8q_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
+    _invoke(lib.fp8q_gemm, (_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
                          _stream(stream, a_q.device)), "fp8q_gemm")
 
 
 def fp8q_gemm_precise(a_q, a_s, w_q, w_s, c, stream=None):
     """fp8q_gemm with each chunk partial formed by FP16 MFMAs on the widened codes."""
     M, N, K, out = _gemm_args("fp8q_gemm_precise", a_q, a_s, w_q, w_s, c)
-    _check(lib.fp8q_gemm_precise(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c),
+    _invoke(lib.fp8q_gemm_precise, (_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c),
                                  out, _stream(stream, a_q.device)), "fp8q_gemm_precise")
 
 
@@ -220,19 +262,17 @@ def _grouped_args(where, a_q, a_s, off, w_q, w_s, c):
 def fp8q_grouped_gemm(a_q, a_s, off, w_q, w_s, c, stream=None):
     """Rows [off[e], off[e+1]) of a_q times expert e's w_q[e]; off is a device int32[G+1]."""
     M_total, G, N, K, out = _grouped_args("fp8q_grouped_gemm", a_q, a_s, off, w_q, w_s, c)
-    _check(lib.fp8q_grouped_gemm(_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
-                                 _ptr(w_s), N, K, _ptr(c), out, _stream(stream, a_q.device)),
-           "fp8q_grouped_gemm")
+    _invoke(lib.fp8q_grouped_gemm, (_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
+                                 _ptr(w_s), N, K, _ptr(c), out, _stream(stream, a_q.device)), "fp8q_grouped_gemm")
 
 
 def fp8q_grouped_gemm_precise(a_q, a_s, off, w_q, w_s, c, stream=None):
     """fp8q_grouped_gemm in the precise mode (FP16 MFMAs on the widened codes)."""
     M_total, G, N, K, out = _grouped_args("fp8q_grouped_gemm_precise", a_q, a_s, off, w_q, w_s,
                                           c)
-    _check(lib.fp8q_grouped_gemm_precise(_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
+    _invoke(lib.fp8q_grouped_gemm_precise, (_ptr(a_q), _ptr(a_s), M_total, _ptr(off), G, _ptr(w_q),
                                          _ptr(w_s), N, K, _ptr(c), out,
-                                         _stream(stream, a_q.device)),
-           "fp8q_grouped_gemm_precise")
+                                         _stream(stream, a_q.device)), "fp8q_grouped_gemm_precise")
 
 
 def fp8q_gemm_fused(x, w_q, w_s, c, mode="f32", stream=None):
@@ -247,7 +287,7 @@ def fp8q_gemm_fused(x, w_q, w_s, c, mode="f32", stream=None):
     _req(wh, "w_s", w_s, ["f32"], (N // GROUP, K // GROUP), x.device)
     _req(wh, "c", c, ["f32", "bf16"], (M, N), x.device)
     out = _out_code(wh, c)
-    _check(lib.fp8q_gemm_fused(_ptr(x), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
+    _invoke(lib.fp8q_gemm_fused, (_ptr(x), _ptr(w_q), _ptr(w_s), M, N, K, _ptr(c), out,
                                _MODES[mode], _stream(stream, x.device)), "fp8q_gemm_fused")
 
 
@@ -264,10 +304,9 @@ def fp8q_grouped_gemm_fused(x, off, w_q, w_s, c, mode="f32", stream=None):
     _req(wh, "w_s", w_s, ["f32"], (G, N // GROUP, K // GROUP), x.device)
     _req(wh, "c", c, ["f32", "bf16"], (M_total, N), x.device)
     out = _out_code(wh, c)
-    _check(lib.fp8q_grouped_gemm_fused(_ptr(x), M_total, _ptr(off), G, _ptr(w_q), _ptr(w_s), N,
+    _invoke(lib.fp8q_grouped_gemm_fused, (_ptr(x), M_total, _ptr(off), G, _ptr(w_q), _ptr(w_s), N,
                                        K, _ptr(c), out, _MODES[mode],
-                                       _stream(stream, x.device)),
-           "fp8q_grouped_gemm_fused")
+                                       _stream(stream, x.device)), "fp8q_grouped_gemm_fused")
 
 
 def fp8q_gemm_bf16(a, w, c, stream=None):
@@ -280,8 +319,7 @@ def fp8q_gemm_bf16(a, w, c, stream=None):
     _req(wh, "w", w, ["bf16"], (N, K), a.device)
     _req(wh, "c", c, ["f32", "bf16"], (M, N), a.device)
     out = _out_code(wh, c)
-    _check(lib.fp8q_gemm_bf16(_ptr(a), _ptr(w), M, N, K, _ptr(c), out, _stream(stream, a.device)),
-           "fp8q_gemm_bf16")
+    _invoke(lib.fp8q_gemm_bf16, (_ptr(a), _ptr(w), M, N, K, _ptr(c), out, _stream(stream, a.device)), "fp8q_gemm_bf16")
 
 
 def fp8q_quantize_act_t(x, q_t, s_t, mode="f32", stream=None):
@@ -292,7 +330,7 @@ def fp8q_quantize_act_t(x, q_t, s_t, mode="f32", stream=None):
     _req(wh, "x", x, ["bf16"], (M, K), x.device)
     _req(wh, "q_t", q_t, ["u8"], (K, M), x.device)
     _req(wh, "s_t", s_t, ["f32"], (M // GROUP, K), x.device)
-    _check(lib.fp8q_quantize_act_t(_ptr(x), M, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
+    _invoke(lib.fp8q_quantize_act_t, (_ptr(x), M, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
                                    _stream(stream, x.device)), "fp8q_quantize_act_t")
 
 
@@ -304,7 +342,7 @@ def fp8q_quantize_weight_t(w, q_t, s_t, mode="f32", stream=None):
     _req(wh, "w", w, ["bf16"], (N, K), w.device)
     _req(wh, "q_t", q_t, ["u8"], (K, N), w.device)
     _req(wh, "s_t", s_t, ["f32"], (K // GROUP, N // GROUP), w.device)
-    _check(lib.fp8q_quantize_weight_t(_ptr(w), N, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
+    _invoke(lib.fp8q_quantize_weight_t, (_ptr(w), N, K, _ptr(q_t), _ptr(s_t), _MODES[mode],
                                       _stream(stream, w.device)), "fp8q_quantize_weight_t")
 
 
@@ -324,16 +362,15 @@ def _rowscaled_args(where, a_q, a_s, b_q, b_s, c):
 def fp8q_gemm_rowscaled(a_q, a_s, b_q, b_s, c, stream=None):
     """c[M][N] = a_q[M][K] x b_q[N][K]^T with 1x128 row-group scales on both."""
     M, N, K, out = _rowscaled_args("fp8q_gemm_rowscaled", a_q, a_s, b_q, b_s, c)
-    _check(lib.fp8q_gemm_rowscaled(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K, _ptr(c),
+    _invoke(lib.fp8q_gemm_rowscaled, (_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K, _ptr(c),
                                    out, _stream(stream, a_q.device)), "fp8q_gemm_rowscaled")
 
 
 def fp8q_gemm_rowscaled_precise(a_q, a_s, b_q, b_s, c, stream=None):
     """fp8q_gemm_rowscaled in the precise mode (FP16 MFMAs on the widened codes)."""
     M, N, K, out = _rowscaled_args("fp8q_gemm_rowscaled_precise", a_q, a_s, b_q, b_s, c)
-    _check(lib.fp8q_gemm_rowscaled_precise(_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K,
-                                           _ptr(c), out, _stream(stream, a_q.device)),
-           "fp8q_gemm_rowscaled_precise")
+    _invoke(lib.fp8q_gemm_rowscaled_precise, (_ptr(a_q), _ptr(a_s), _ptr(b_q), _ptr(b_s), M, N, K,
+                                           _ptr(c), out, _stream(stream, a_q.device)), "fp8q_gemm_rowscaled_precise")
 
 
 # ---------------------------------------------------------- allocation helpers
