@@ -462,23 +462,34 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
+def recorded(kind, kernel, cfg):
+    """The fields of the committed `kind` record line ("traffic-record" or
+    "clock-record") of profiles/*.md for this kernel and workload, or None if
+    there is none or the GEMM code changed since it was measured."""
+    import glob
+    digest = kernel_source_digest()
+    workload = cfg["workload"].split(":")[0]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if not line.startswith(kind + ":"):
+                continue
+            rec = dict(kv.split("=", 1) for kv in line.split(":", 1)[1].split())
+            if (rec.get("kernel") == kernel and rec.get("workload") == workload
+                    and rec.get("source_sha256") == digest):
+                return rec
+    return None
+
+
 def recorded_traffic(kernel, cfg):
     """HBM-side bytes per launch from the committed rocprofv3 --pmc summary
     (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), or None
     if there is none for this kernel and workload or the kernel changed."""
-    import glob
-    digest = kernel_source_digest()
-    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
-        rec = {}
-        for line in open(path):
-            if line.startswith("traffic-record:"):
-                for kv in line.split(":", 1)[1].split():
-                    k, v = kv.split("=", 1)
-                    rec[k] = v
-        if (rec.get("kernel") == kernel and rec.get("workload") == cfg["workload"].split(":")[0]
-                and rec.get("source_sha256") == digest):
-            return float(rec["bytes_per_launch"])
-    return None
+    rec = recorded("traffic-record", kernel, cfg)
+    return float(rec["bytes_per_launch"]) if rec else None
+
+
+# ------------------------------------------------------------ shader clock
+PEAK_CLOCK_MHZ = 2400.0   # the clock the published MFMA peaks assume
 
 
 # --------------------------------------------------------------- cpu baseline
@@ -738,6 +749,23 @@ def main():
         roof = {"kernel": "fp8q_grouped_gemm", "bound": "hbm", "achieved": dom["GB_s"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dom["GB_s"] / PEAK_HBM_GBS,
                 "traffic": recorded_traffic("fp8q_grouped_gemm", cfg)}
+
+    # Clock-normalised figures: the shader clock the dominant kernel holds,
+    # from its committed rocprofv3 counter record (GRBM_GUI_ACTIVE per XCD over
+    # the dispatch's duration; reported while the GEMM code is unchanged),
+    # and its per-launch median beside the back-to-back average the fraction
+    # is based on.
+    clk = recorded("clock-record", roof["kernel"], cfg)
+    if clk:
+        roof["sclk_MHz_profiled"] = float(clk["sclk_MHz"])
+        roof["mfma_busy_profiled"] = float(clk["mfma_busy"])
+        if roof["unit"] == "TFLOP/s":
+            roof["peak_at_sclk"] = roof["peak"] * roof["sclk_MHz_profiled"] / PEAK_CLOCK_MHZ
+            roof["frac_at_sclk"] = roof["achieved"] / roof["peak_at_sclk"]
+    med = dom.get("median_us")
+    if med:
+        roof["median_launch_us"] = med
+        roof["frac_by_median_launch"] = roof["frac"] * dom["avg_us"] / med
 
     value = flops / (ms_per_step * 1e-3) / 1e12
     bf16 = args.workload == "bf16"
