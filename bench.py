@@ -73,6 +73,9 @@ def parse():
     p.add_argument("--stream-ceiling", action="store_true",
                    help="only time the streaming probe (16 B read, 8 B written per lane: the "
                         "quantizers' 2:1 traffic) at the quantizers' sizes: their HBM ceiling")
+    p.add_argument("--mix-probe", action="store_true",
+                   help="only time the instruction-mix probe: MFMA streams with the GEMM main "
+                        "loop's LDS fragment reads, promotion FMAs and FP8->FP16 widening")
     return p.parse_args()
 
 
@@ -157,6 +160,62 @@ def stream_ceiling(steps, rounds=10):
         torch.cuda.synchronize()
     print(json.dumps({"stream_ceiling": out, "steps": steps, "rounds": rounds,
                       "input_sets": "4 (1 at >= 1 GiB)"}))
+
+
+MIX_KINDS = [  # (kind bits, what one iteration issues per wave)
+    (0, "FP8: 4 MFMA 16x16x128 chained through C"),
+    (1, "FP8: + 3 LDS reads (16 B) feeding the next operands"),
+    (2, "FP8: MFMA from zero + 16 promotion FMAs"),
+    (3, "FP8: + 3 LDS reads + 16 promotion FMAs (the fp8q_gemm mix)"),
+    (8, "FP16: 16 MFMA 16x16x32, 4 chained per block"),
+    (9, "FP16: + 3 LDS reads"),
+    (10, "FP16: + 16 promotion FMAs"),
+    (11, "FP16: + 3 LDS reads + 16 promotion FMAs"),
+    (13, "FP16: + 3 LDS reads widened by 24 FP8->FP16 conversions"),
+    (15, "FP16: + reads + 24 conversions + 16 FMAs (the fp8q_gemm_precise mix)"),
+]
+
+
+def mix_probe(iters=20000, rounds=5):
+    """The instruction-mix probe of libfp8q_probe.so (one workgroup of 8 waves
+    per CU, two waves per SIMD): for each mix, the median over `rounds` of one
+    launch's duration (HIP events) divided by `iters`, i.e. ns per iteration
+    per wave; `mfma_share` = the time of the same mode's MFMA-only mix over
+    this mix's time, the share of the matrix core's time that survives."""
+    import ctypes
+    import torch
+    L = _probe_lib()
+    L.fp8q_probe_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.fp8q_probe_mix.restype = ctypes.c_int
+    L.fp8q_probe_cus.restype = ctypes.c_int
+    cus = L.fp8q_probe_cus()
+    if cus <= 0:
+        raise RuntimeError("fp8q_probe_cus failed")
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run(kind, n):
+        st = L.fp8q_probe_mix(kind, n, ctypes.c_void_p(out.data_ptr()), stream)
+        if st != 0:
+            raise RuntimeError(f"fp8q_probe_mix({kind}) failed: {st}")
+
+    ns = {}
+    for r in range(rounds):
+        for kind, _ in MIX_KINDS:
+            run(kind, 100)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(kind, iters)
+            e1.record()
+            torch.cuda.synchronize()
+            ns.setdefault(kind, []).append(e0.elapsed_time(e1) * 1e6 / iters)
+    rows = []
+    for kind, what in MIX_KINDS:
+        t = float(np.median(ns[kind]))
+        t0 = float(np.median(ns[kind & 8]))
+        rows.append({"kind": kind, "mix": what, "ns_per_iter_per_wave": t, "mfma_share": t0 / t})
+    print(json.dumps({"mix_probe": rows, "iters": iters, "rounds": rounds, "workgroups": cus,
+                      "waves_per_simd": 2}))
 
 
 def gemm_bytes(M, N, K, out_bytes):
@@ -617,6 +676,9 @@ def main():
         return
     if args.stream_ceiling:
         stream_ceiling(args.steps)
+        return
+    if args.mix_probe:
+        mix_probe()
         return
     import torch
     import fine_grained_block_fp8q_amd as fq

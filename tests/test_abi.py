@@ -252,3 +252,22 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert lib.fp8q_gemm_precise(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
     assert lib.fp8q_grouped_gemm_precise(A, A, 8, A, 2, A, A, 128, 128, A, 0, None) == E_DEVICE
     assert lib.fp8q_gemm_rowscaled_precise(A, A, A, A, 4, 128, 128, A, 0, None) == E_DEVICE
+
+
+def test_probe_library_exports_and_validation():
+    """The measurement probes (streaming ceiling, instruction mix) load and
+    reject invalid arguments on the host before any HIP call."""
+    path = os.path.join(ROOT, "fine_grained_block_fp8q_amd", "libfp8q_probe.so")
+    if not os.path.exists(path):
+        pytest.fail("libfp8q_probe.so is not built (python fine_grained_block_fp8q_amd/build.py)")
+    L = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    L.fp8q_probe_stream.argtypes = [p, p, ctypes.c_int64, ctypes.c_int, p]
+    L.fp8q_probe_mix.argtypes = [ctypes.c_int, ctypes.c_int, p, p]
+    for name in ("fp8q_probe_stream", "fp8q_probe_mix", "fp8q_probe_cus"):
+        assert hasattr(L, name)
+    assert L.fp8q_probe_stream(None, None, 1024, 1, None) == -1
+    assert L.fp8q_probe_stream(p(4096), p(8192), 1000, 1, None) == -1   # not a multiple of 16
+    assert L.fp8q_probe_stream(p(4096), p(8192), 1024, 3, None) == -1   # ratio
+    assert L.fp8q_probe_mix(0, 100, None, None) == -1
+    assert L.fp8q_probe_mix(0, 0, p(4096), None) == -1
