@@ -555,6 +555,15 @@ PEAK_CLOCK_MHZ = 2400.0   # the clock the published MFMA peaks assume
 
 # --------------------------------------------------------------- cpu baseline
 def _cpu_model():
+    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
