@@ -142,6 +142,10 @@ fp8q_status fp8q_quantize_weight(const void* w_bf16, int64_t N, int64_t K,
  *   s_a * s_w and of the promotion per chunk).  T is what the matrix core
  * can lose; it can exceed the 1e-5 * S tolerance where one product dominates
  * an 8-K group (an outlier channel).  fp8q_gemm_precise meets the tolerance.
+ * RANGE (both modes): the bounds assume every product s_a * s_w is a normal
+ * FP32 number (>= 2^-126) and no partial sum overflows; outside that range
+ * the FP32 arithmetic of the promotion itself loses precision (a subnormal
+ * s_a * s_w keeps fewer significant bits).
  */
 fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s,
                       const uint8_t* w_q, const float* w_s,
@@ -164,7 +168,7 @@ fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s,
  *   |C - C_exact| <= (G + 34) * 2^-24 * S  (+ half a BF16 ulp of C_exact),
  * which is within the 1e-5 * S tolerance for K <= 17024 (G <= 133); on
  * random data the error stays near 1e-7 * S at any K (8192 x 8192 x 65536
- * measured: 1.4e-8 * S).
+ * measured: 1.4e-8 * S).  The RANGE clause of fp8q_gemm applies.
  */
 fp8q_status fp8q_gemm_precise(const uint8_t* a_q, const float* a_s,
                               const uint8_t* w_q, const float* w_s,
