@@ -36,7 +36,9 @@
  *   - Inputs must be finite; outputs must not alias inputs.
  *   - E4M3 here is the OCP "E4M3FN" encoding (bias 7, no infinities, max 448).
  *   - Thread-safe; the only global state is a per-device architecture cache
- *     (and, in FP8Q_DEBUG_CHECKS builds, a per-device offsets-error flag).
+ *     (and, in FP8Q_DEBUG_CHECKS builds, a per-device offsets-error flag:
+ *     grouped calls on one device that overlap in time share it, so one of
+ *     them may report the other's invalid offsets).
  */
 #ifndef FP8Q_H
 #define FP8Q_H
