@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--mix-probe", action="store_true",
                    help="only time the instruction-mix probe: MFMA streams with the GEMM main "
                         "loop's LDS fragment reads, promotion FMAs and FP8->FP16 widening")
+    p.add_argument("--ring-probe", action="store_true",
+                   help="only time the ring-streaming probe: the grouped GEMM's operand "
+                        "pipeline alone (no MFMA) for its tile shapes and ring depths")
     return p.parse_args()
 
 
@@ -216,6 +219,64 @@ def mix_probe(iters=20000, rounds=5):
         rows.append({"kind": kind, "mix": what, "ns_per_iter_per_wave": t, "mfma_share": t0 / t})
     print(json.dumps({"mix_probe": rows, "iters": iters, "rounds": rounds, "workgroups": cus,
                       "waves_per_simd": 2}))
+
+
+RING_SHAPES = [  # (activation rows per tile, ring stages): the grouped GEMM's tiles
+    (0, 2), (0, 3), (0, 4), (64, 3), (128, 3), (160, 3), (192, 2), (256, 2)]
+
+
+def ring_probe(rounds=5):
+    """The ring-streaming probe of libfp8q_probe.so: one workgroup per CU
+    streams tiles of 256 weight rows of its own plus `ra` activation rows
+    shared by the 16 tiles of an expert, K = 7168, through an LDS ring of
+    `stages` stages, with no MFMA.  Two regimes: 16 tiles per CU (7.5 GB of
+    weights, the MoE batch's volume) and 2 tiles per CU (0.94 GB, the decode
+    batch's).  Median over `rounds` launches (HIP events); weight GB/s counts
+    the weight bytes, total GB/s adds the activation bytes each tile reads."""
+    import ctypes
+    import torch
+    L = _probe_lib()
+    L.fp8q_probe_ring.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.fp8q_probe_ring.restype = ctypes.c_int
+    L.fp8q_probe_cus.restype = ctypes.c_int
+    cus = L.fp8q_probe_cus()
+    K, per_expert = 7168, 16
+    w = torch.empty((cus * 16 * 256, K), dtype=torch.uint8, device="cuda:0")
+    a = torch.empty((256 * 256, K), dtype=torch.uint8, device="cuda:0")
+    w.fill_(0x38)
+    a.fill_(0x38)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rows = []
+    for tiles in (16, 2):
+        w_rows = cus * tiles * 256
+        for ra, stages in RING_SHAPES:
+            a_rows = 256 * ra if ra else 0
+
+            def run():
+                st = L.fp8q_probe_ring(ctypes.c_void_p(w.data_ptr()), w_rows,
+                                       ctypes.c_void_p(a.data_ptr()), a_rows, K, ra, stages,
+                                       tiles, per_expert, stream)
+                if st != 0:
+                    raise RuntimeError(f"fp8q_probe_ring({ra}, {stages}) failed: {st}")
+
+            run()
+            ts = []
+            for _ in range(rounds):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = float(np.median(ts))
+            wb = cus * tiles * 256 * K
+            ab = cus * tiles * ra * K
+            rows.append({"tiles_per_cu": tiles, "act_rows": ra, "stages": stages, "us": us,
+                         "weight_GB_s": wb / us / 1e3, "total_GB_s": (wb + ab) / us / 1e3})
+    print(json.dumps({"ring_probe": rows, "K": K, "weight_rows_per_tile": 256,
+                      "tiles_per_expert": per_expert, "workgroups": cus, "rounds": rounds}))
 
 
 def gemm_bytes(M, N, K, out_bytes):
@@ -541,6 +602,21 @@ def recorded(kind, kernel, cfg):
     return None
 
 
+def recorded_ceiling(kernel, cfg):
+    """Algorithmic GB/s of the workload's tile shapes streamed without
+    arithmetic (the `ceiling-record` lines of profiles/*.md, written from
+    bench.py --ring-probe), or None."""
+    import glob
+    workload = cfg["workload"].split(":")[0]
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if line.startswith("ceiling-record:"):
+                rec = dict(kv.split("=", 1) for kv in line.split(":", 1)[1].split())
+                if rec.get("kernel") == kernel and rec.get("workload") == workload:
+                    return float(rec["GB_s"])
+    return None
+
+
 def recorded_traffic(kernel, cfg):
     """HBM-side bytes per launch from the committed rocprofv3 --pmc summary
     (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), or None
@@ -688,6 +764,9 @@ def main():
         return
     if args.mix_probe:
         mix_probe()
+        return
+    if args.ring_probe:
+        ring_probe()
         return
     import torch
     import fine_grained_block_fp8q_amd as fq
@@ -841,6 +920,13 @@ def main():
         if roof["unit"] == "TFLOP/s":
             roof["peak_at_sclk"] = roof["peak"] * roof["sclk_MHz_profiled"] / PEAK_CLOCK_MHZ
             roof["frac_at_sclk"] = roof["achieved"] / roof["peak_at_sclk"]
+    # The streaming ceiling of an HBM-bound kernel's tile shapes, from the
+    # committed ring-probe summary (the probe, not the GEMM, measures it).
+    if roof["unit"] == "GB/s":
+        ceil = recorded_ceiling(roof["kernel"], cfg)
+        if ceil:
+            roof["stream_ceiling_GB_s"] = ceil
+            roof["frac_of_stream_ceiling"] = roof["achieved"] / ceil
     med = dom.get("median_us")
     if med:
         roof["median_launch_us"] = med

@@ -114,9 +114,10 @@ def bind(fn, *args, **kwargs):
     """Validate a call once and return a zero-argument callable that repeats
     it: the same C entry point with the same pointers, sizes and stream, and
     none of the per-call host checks (for launch loops whose kernels are
-    shorter than those checks).  The tensors must stay alive and keep their
-    storage while the callable is used; a non-OK status still raises.
-    Example: run = bind(fp8q_quantize_act, x, q, s); run(); run()."""
+    shorter than those checks).  The callable holds references to the
+    arguments, so their tensors stay alive while it exists; they must keep
+    their storage (no resize or set_) while it is used.  A non-OK status
+    still raises.  Example: run = bind(fp8q_quantize_act, x, q, s); run(); run()."""
     _capture.on = True
     try:
         fn(*args, **kwargs)
@@ -127,10 +128,13 @@ def bind(fn, *args, **kwargs):
     finally:
         _capture.on = False
 
+    keep = (args, kwargs)   # the pointers in cargs refer to these tensors' storage
+
     def run():
         st = cfunc(*cargs)
         if st != OK:
             raise Fp8qError(st, where)
+    run.args = keep
     return run
 
 

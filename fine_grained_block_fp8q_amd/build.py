@@ -89,6 +89,7 @@ def _build_probe(verbose):
     tmp = LIB_PROBE + ".tmp"
     out = _run([HIPCC, *COMMON, "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-shared",
                 os.path.join(CSRC, "stream_probe.hip"), os.path.join(CSRC, "mix_probe.hip"),
+                os.path.join(CSRC, "ring_probe.hip"),
                 "-o", tmp])
     if verbose and out.strip():
         print(out)

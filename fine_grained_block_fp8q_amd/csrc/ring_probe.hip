@@ -1,0 +1,149 @@
+// Ring-streaming probe (measurement support, not part of the method): the
+// rate at which the grouped GEMM's operand pipeline alone can stream expert
+// weights, for the ring depths and activation-row counts its tiles use.
+// Built into libfp8q_probe.so; bench.py --ring-probe calls it.
+//
+// One workgroup of 8 waves per CU walks `tiles_per_wg` tiles.  Tile t reads
+// 256 weight rows of its own (rows 256 t .. 256 t + 255 of W, wrapping) and
+// RA activation rows shared by the `tiles_per_expert` consecutive tiles of
+// one expert, 128 bytes of each row per K chunk, into an LDS ring of S
+// stages with the GEMM's 16-byte direct-to-LDS buffer loads (1 KiB per
+// instruction: 8 rows of 128 bytes), the instructions of a chunk split evenly
+// over the waves.  Per chunk: issue chunk g + S - 1, wait until chunk g has
+// landed, one barrier.  No MFMA and no LDS reads: what it measures is the
+// streaming ceiling of the tile shape, S - 1 chunks in flight per CU.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_common.hpp"
+
+namespace fp8q_ring_probe {
+
+using fp8q::make_rsrc;
+using fp8q::to_lds;
+using fp8q::wait_vmcnt;
+
+constexpr int kWRows = 256;
+
+template <int RA, int S>
+struct Ring {
+  static constexpr int A_INSTR = RA / 8;              // 1 KiB instructions per chunk
+  static constexpr int W_INSTR = kWRows / 8;
+  static constexpr int INSTR = A_INSTR + W_INSTR;
+  static constexpr int PER_WAVE = (INSTR + 7) / 8;    // the last ones repeat A or W loads
+  static constexpr int STAGE = INSTR * 1024;
+  // at least 96 KiB, so that a second workgroup never shares the CU
+  static constexpr int LDS = S * STAGE > 96 * 1024 ? S * STAGE : 96 * 1024;
+  static_assert(RA % 8 == 0 && RA <= 256 && S >= 2, "shape");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(PER_WAVE * (S - 1) < 64, "vmcnt range");
+};
+
+// Chunk g's loads of this wave into its stage (chunks past the end re-fetch
+// the last one).
+template <int RA, int S>
+__device__ __forceinline__ void issue_chunk(uint8_t* lds, __amdgpu_buffer_rsrc_t ra,
+                                            __amdgpu_buffer_rsrc_t rw, const uint32_t* voff,
+                                            const int* dst, const bool* is_a, int64_t g,
+                                            int64_t G) {
+  using R = Ring<RA, S>;
+  const int64_t gc = g < G ? g : G - 1;
+  uint8_t* stage = lds + (int)(g % S) * R::STAGE;
+#pragma unroll
+  for (int j = 0; j < R::PER_WAVE; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a[j] ? ra : rw, to_lds(stage + dst[j]), 16,
+                                             voff[j], (int)(gc * 128), 0, 0);
+}
+
+template <int RA, int S>
+__global__ __launch_bounds__(512) void ring_kernel(const uint8_t* __restrict__ W, int64_t w_rows,
+                                                   const uint8_t* __restrict__ A, int64_t a_rows,
+                                                   int64_t K, int tiles_per_wg,
+                                                   int tiles_per_expert) {
+  using R = Ring<RA, S>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[R::LDS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t G = K / 128;
+  for (int i = 0; i < tiles_per_wg; ++i) {
+    const int64_t tile = blockIdx.x + (int64_t)i * gridDim.x;
+    const int64_t w0 = (tile * kWRows) % w_rows;
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + w0 * K, kWRows * K);
+    __amdgpu_buffer_rsrc_t ra = rw;
+    if constexpr (RA > 0) {
+      const int64_t a0 = ((tile / tiles_per_expert) * RA) % a_rows;
+      ra = make_rsrc(A + a0 * K, RA * K);
+    }
+    uint32_t voff[R::PER_WAVE];
+    int dst[R::PER_WAVE];
+    bool is_a[R::PER_WAVE];
+#pragma unroll
+    for (int j = 0; j < R::PER_WAVE; ++j) {
+      const int m = (wave * R::PER_WAVE + j) % R::INSTR;
+      is_a[j] = m < R::A_INSTR;
+      const int r = (is_a[j] ? m : m - R::A_INSTR) * 8 + (lane >> 3);
+      voff[j] = (uint32_t)(r * K) + (uint32_t)((lane & 7) * 16);
+      dst[j] = m * 1024;
+    }
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) issue_chunk<RA, S>(lds, ra, rw, voff, dst, is_a, s, G);
+    for (int64_t g = 0; g < G; ++g) {
+      issue_chunk<RA, S>(lds, ra, rw, voff, dst, is_a, g + S - 1, G);
+      wait_vmcnt<R::PER_WAVE * (S - 1)>();  // chunk g landed
+      __builtin_amdgcn_s_barrier();
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  }
+}
+
+template <int RA, int S>
+hipError_t launch(const uint8_t* W, int64_t w_rows, const uint8_t* A, int64_t a_rows, int64_t K,
+                  int blocks, int tiles_per_wg, int tiles_per_expert, hipStream_t stream) {
+  ring_kernel<RA, S><<<dim3(blocks), dim3(512), 0, stream>>>(W, w_rows, A, a_rows, K,
+                                                             tiles_per_wg, tiles_per_expert);
+  return hipGetLastError();
+}
+
+}  // namespace fp8q_ring_probe
+
+using fp8q_ring_probe::kWRows;
+using fp8q_ring_probe::launch;
+
+extern "C" {
+
+// Streams tiles through the ring described above on one workgroup per CU of
+// the current device.  W: device [w_rows][K] bytes, w_rows a multiple of 256;
+// A: device [a_rows][K] bytes, a_rows a multiple of ra (A unused when ra is
+// 0); K a multiple of 128 with 256 * K < 2^31; (ra, stages) one of (0, 2),
+// (0, 3), (0, 4), (64, 3), (128, 3), (160, 3), (192, 2), (256, 2): the
+// grouped GEMM's row buckets with their ring depths, and weights alone.  Returns 0, -1 for
+// unsupported arguments, or the HIP error code.  Asynchronous on `stream`.
+int fp8q_probe_ring(const void* W, int64_t w_rows, const void* A, int64_t a_rows, int64_t K,
+                    int ra, int stages, int tiles_per_wg, int tiles_per_expert,
+                    hipStream_t stream) {
+  if (!W || w_rows <= 0 || w_rows % kWRows || K <= 0 || K % 128 || kWRows * K >= (1ll << 31) ||
+      tiles_per_wg <= 0 || tiles_per_expert <= 0 ||
+      (ra > 0 && (!A || a_rows < ra || a_rows % ra || (int64_t)ra * K >= (1ll << 31))))
+    return -1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return (int)hipGetLastError();
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  const uint8_t* a = static_cast<const uint8_t*>(A);
+  hipError_t e;
+  if (ra == 0 && stages == 2) e = launch<0, 2>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 0 && stages == 3) e = launch<0, 3>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 0 && stages == 4) e = launch<0, 4>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 64 && stages == 3) e = launch<64, 3>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 128 && stages == 3) e = launch<128, 3>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 160 && stages == 3) e = launch<160, 3>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 192 && stages == 2) e = launch<192, 2>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else if (ra == 256 && stages == 2) e = launch<256, 2>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
+  else return -1;
+  return (int)e;
+}
+
+}  // extern "C"

@@ -264,8 +264,14 @@ def test_probe_library_exports_and_validation():
     p = ctypes.c_void_p
     L.fp8q_probe_stream.argtypes = [p, p, ctypes.c_int64, ctypes.c_int, p]
     L.fp8q_probe_mix.argtypes = [ctypes.c_int, ctypes.c_int, p, p]
-    for name in ("fp8q_probe_stream", "fp8q_probe_mix", "fp8q_probe_cus"):
+    L.fp8q_probe_ring.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, p]
+    for name in ("fp8q_probe_stream", "fp8q_probe_mix", "fp8q_probe_cus", "fp8q_probe_ring"):
         assert hasattr(L, name)
+    assert L.fp8q_probe_ring(None, 256, None, 0, 7168, 0, 2, 1, 16, None) == -1
+    assert L.fp8q_probe_ring(p(4096), 100, None, 0, 7168, 0, 2, 1, 16, None) == -1   # w_rows
+    assert L.fp8q_probe_ring(p(4096), 256, None, 128, 7168, 128, 3, 1, 16, None) == -1  # no A
+    assert L.fp8q_probe_ring(p(4096), 256, p(8192), 200, 7168, 128, 3, 1, 16, None) == -1
     assert L.fp8q_probe_stream(None, None, 1024, 1, None) == -1
     assert L.fp8q_probe_stream(p(4096), p(8192), 1000, 1, None) == -1   # not a multiple of 16
     assert L.fp8q_probe_stream(p(4096), p(8192), 1024, 3, None) == -1   # ratio

@@ -86,3 +86,22 @@ def test_bind_validates_once_and_returns_the_call():
         run = fq.bind(fq.fp8q_quantize_act, x, q, s)
         with pytest.raises(fq.Fp8qError):
             run()
+
+
+def test_bind_keeps_its_tensors_alive():
+    """The bound call's pointers stay valid: the callable holds the tensors,
+    which are freed only with it."""
+    import gc
+    import weakref
+    M, K = 32, 256
+    x, q, s = _t((M, K), bf16), _t((M, K), u8), _t((K // 128, M), f32)
+    refs = [weakref.ref(t) for t in (x, q, s)]
+    with um.patch.object(fq.lib, "fp8q_quantize_act", lambda *a: 0):
+        run = fq.bind(fq.fp8q_quantize_act, x, q, s)
+        del x, q, s
+        gc.collect()
+        assert all(r() is not None for r in refs)
+        run()
+    del run
+    gc.collect()
+    assert all(r() is None for r in refs)
