@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--workload", default="dense",
                    choices=["dense", "moe", "decode", "largek", "bf16", "backward", "dense_fused",
                             "decode_fused"])
+    p.add_argument("--mfma-scaled", action="store_true",
+                   help="dense / largek: power-of-two scales, applied by the matrix core "
+                        "(fp8q_gemm_mfma_scaled), timed beside fp8q_gemm on the same operands")
     p.add_argument("--precise", action="store_true",
                    help="the precise GEMM calls (fp8q_gemm_precise, fp8q_grouped_gemm_precise, "
                         "fp8q_gemm_rowscaled_precise) in place of the FP8-MFMA ones")
@@ -170,6 +173,8 @@ MIX_KINDS = [  # (kind bits, what one iteration issues per wave)
     (1, "FP8: + 3 LDS reads (16 B) feeding the next operands"),
     (2, "FP8: MFMA from zero + 16 promotion FMAs"),
     (3, "FP8: + 3 LDS reads + 16 promotion FMAs (the fp8q_gemm mix)"),
+    (16, "FP8 with E8M0 operand scales: 4 MFMA chained through C"),
+    (19, "FP8 with E8M0 scales: + reads + promotion (the fp8q_gemm_mfma_scaled mix)"),
     (8, "FP16: 16 MFMA 16x16x32, 4 chained per block"),
     (9, "FP16: + 3 LDS reads"),
     (10, "FP16: + 16 promotion FMAs"),
@@ -215,7 +220,7 @@ def mix_probe(iters=20000, rounds=5):
     rows = []
     for kind, what in MIX_KINDS:
         t = float(np.median(ns[kind]))
-        t0 = float(np.median(ns[kind & 8]))
+        t0 = float(np.median(ns[kind & 8]))   # the unscaled MFMA-only stream of the mode
         rows.append({"kind": kind, "mix": what, "ns_per_iter_per_wave": t, "mfma_share": t0 / t})
     print(json.dumps({"mix_probe": rows, "iters": iters, "rounds": rounds, "workgroups": cus,
                       "waves_per_simd": 2}))
@@ -284,7 +289,7 @@ def gemm_bytes(M, N, K, out_bytes):
 
 
 # --------------------------------------------------------------------- setup
-def setup_dense(fq, torch, name, sets, fused=False, precise=False):
+def setup_dense(fq, torch, name, sets, fused=False, precise=False, mfma_scaled=False):
     import workloads
     c = workloads.WORKLOADS[name]
     M, N, K = c["M"], c["N"], c["K"]
@@ -308,10 +313,13 @@ def setup_dense(fq, torch, name, sets, fused=False, precise=False):
     # per-call host checks (fq.bind): the launch loops below must not be
     # host-bound for the shorter kernels
     calls = {n: [] for n in ("fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm_fused",
-                             "fp8q_gemm_precise", "fp8q_gemm")}
+                             "fp8q_gemm_precise", "fp8q_gemm_mfma_scaled", "fp8q_gemm")}
+    mode = "pow2" if mfma_scaled else "f32"
     for A, W, aq, as_, wq, ws, C in bufs:
-        calls["fp8q_quantize_act"].append(fq.bind(fq.fp8q_quantize_act, A, aq, as_))
-        calls["fp8q_quantize_weight"].append(fq.bind(fq.fp8q_quantize_weight, W, wq, ws))
+        calls["fp8q_quantize_act"].append(fq.bind(fq.fp8q_quantize_act, A, aq, as_, mode))
+        calls["fp8q_quantize_weight"].append(fq.bind(fq.fp8q_quantize_weight, W, wq, ws, mode))
+        calls["fp8q_gemm_mfma_scaled"].append(
+            fq.bind(fq.fp8q_gemm_mfma_scaled, aq, as_, wq, ws, C))
         calls["fp8q_gemm_fused"].append(fq.bind(fq.fp8q_gemm_fused, A, wq, ws, C))
         calls["fp8q_gemm_precise"].append(fq.bind(fq.fp8q_gemm_precise, aq, as_, wq, ws, C))
         calls["fp8q_gemm"].append(fq.bind(fq.fp8q_gemm, aq, as_, wq, ws, C))
@@ -319,7 +327,8 @@ def setup_dense(fq, torch, name, sets, fused=False, precise=False):
     def launch(name, i):
         calls[name][i % sets]()
 
-    gname = "fp8q_gemm_precise" if precise else "fp8q_gemm"
+    gname = ("fp8q_gemm_precise" if precise else
+             "fp8q_gemm_mfma_scaled" if mfma_scaled else "fp8q_gemm")
     order = (["fp8q_quantize_weight", "fp8q_gemm_fused"] if fused else
              ["fp8q_quantize_act", "fp8q_quantize_weight", gname])
 
@@ -336,11 +345,16 @@ def setup_dense(fq, torch, name, sets, fused=False, precise=False):
         kernels.insert(0, ("fp8q_gemm_fused", "mfma", 2.0 * M * N * K, "flop"))
     if precise:
         kernels.insert(0, ("fp8q_gemm_precise", "mfma_wide16", 2.0 * M * N * K, "flop"))
+    if mfma_scaled:
+        kernels.insert(0, ("fp8q_gemm_mfma_scaled", "mfma", 2.0 * M * N * K, "flop"))
     flops = 2.0 * M * N * K
-    tag = name + ("_fused" if fused else "") + ("_precise" if precise else "")
+    tag = (name + ("_fused" if fused else "") + ("_precise" if precise else "")
+           + ("_mfma_scaled" if mfma_scaled else ""))
     how = "quantized inside the GEMM" if fused else "1x128 act quant"
     if precise:
         how += "; precise GEMM (codes widened to FP16, FP16 MFMA)"
+    if mfma_scaled:
+        how += "; power-of-two scales applied by the matrix core (E8M0)"
     cfg = {"workload": f"{tag}: A {M}x{K} bf16 ({how}), W {N}x{K} bf16 "
                        f"(128x128 block quant), C = A W^T fp32",
            "M": M, "N": N, "K": K, "out": "f32", "input_sets": sets}
@@ -753,6 +767,9 @@ def cpu_baseline(name):
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.mfma_scaled and (args.precise or args.workload not in ("dense", "largek")):
+        print(json.dumps({"error": "--mfma-scaled applies to the dense and largek workloads only"}))
+        sys.exit(2)
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -776,7 +793,8 @@ def main():
     base = args.workload.replace("_fused", "")
     fused = base != args.workload
     if base in ("dense", "largek"):
-        step, launch, kernels, flops, cfg = setup_dense(fq, torch, base, sets, fused, args.precise)
+        step, launch, kernels, flops, cfg = setup_dense(fq, torch, base, sets, fused, args.precise,
+                                                        args.mfma_scaled)
     elif args.workload == "bf16":
         step, launch, kernels, flops, cfg = setup_bf16(fq, torch, sets)
     elif args.workload == "backward":
@@ -878,6 +896,13 @@ def main():
                     "fused": dom["avg_us"],
                     "quantize_act_plus_grouped_gemm": (kout["fp8q_quantize_act"]["avg_us"]
                                                        + kout["fp8q_grouped_gemm"]["avg_us"])}}
+    elif args.mfma_scaled and args.workload in ("dense", "largek"):
+        dom = kout["fp8q_gemm_mfma_scaled"]
+        roof = {"kernel": "fp8q_gemm_mfma_scaled", "bound": "mfma", "achieved": dom["TFLOP_s"],
+                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": dom["TFLOP_s"] / PEAK_FP8_TFLOPS,
+                "traffic": recorded_traffic("fp8q_gemm_mfma_scaled", cfg),
+                "vs_fp8q_gemm_same_operands_us": {
+                    "mfma_scaled": dom["avg_us"], "fp8q_gemm": kout["fp8q_gemm"]["avg_us"]}}
     elif args.precise and args.workload in ("dense", "largek"):
         dom = kout["fp8q_gemm_precise"]
         roof = {"kernel": "fp8q_gemm_precise", "bound": "mfma", "achieved": dom["TFLOP_s"],

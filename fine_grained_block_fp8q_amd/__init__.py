@@ -44,6 +44,8 @@ lib.fp8q_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_gemm.restype = _st
 lib.fp8q_gemm_precise.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
 lib.fp8q_gemm_precise.restype = _st
+lib.fp8q_gemm_mfma_scaled.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _i32, _p]
+lib.fp8q_gemm_mfma_scaled.restype = _st
 lib.fp8q_grouped_gemm.argtypes = [_p, _p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32, _p]
 lib.fp8q_grouped_gemm.restype = _st
 lib.fp8q_grouped_gemm_precise.argtypes = [_p, _p, _i64, _p, _i32, _p, _p, _i64, _i64, _p, _i32,
@@ -249,6 +251,14 @@ def fp8q_gemm_precise(a_q, a_s, w_q, w_s, c, stream=None):
                                  out, _stream(stream, a_q.device)), "fp8q_gemm_precise")
 
 
+def fp8q_gemm_mfma_scaled(a_q, a_s, w_q, w_s, c, stream=None):
+    """fp8q_gemm with power-of-two scales applied by the matrix core (E8M0)."""
+    M, N, K, out = _gemm_args("fp8q_gemm_mfma_scaled", a_q, a_s, w_q, w_s, c)
+    _invoke(lib.fp8q_gemm_mfma_scaled, (_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), M, N, K,
+                                     _ptr(c), out, _stream(stream, a_q.device)),
+            "fp8q_gemm_mfma_scaled")
+
+
 def _grouped_args(where, a_q, a_s, off, w_q, w_s, c):
     M_total, K = _dims(where, a_q, 2, "a_q")
     G, N, _ = _dims(where, w_q, 3, "w_q")
@@ -423,11 +433,12 @@ def gemm_rowscaled(a_q, a_s, b_q, b_s, out_dtype=None, stream=None, precise=Fals
     return c
 
 
-def gemm(a_q, a_s, w_q, w_s, out_dtype=None, stream=None, precise=False):
+def gemm(a_q, a_s, w_q, w_s, out_dtype=None, stream=None, precise=False, mfma_scaled=False):
     import torch
     out_dtype = out_dtype or torch.float32
     c = torch.empty((a_q.shape[0], w_q.shape[0]), dtype=out_dtype, device=a_q.device)
-    f = fp8q_gemm_precise if precise else fp8q_gemm
+    assert not (precise and mfma_scaled), "one GEMM mode"
+    f = fp8q_gemm_precise if precise else fp8q_gemm_mfma_scaled if mfma_scaled else fp8q_gemm
     f(a_q, a_s, w_q, w_s, c, stream)
     return c
 

@@ -18,7 +18,7 @@ hipError_t launch_quantize_weight(const void* w, int64_t N, int64_t K, uint8_t* 
                                   int mode, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
                        const float* w_s, int64_t M, int64_t N, int64_t K, void* c, int out_bf16,
-                       int precise, hipStream_t stream);
+                       int mode, hipStream_t stream);
 hipError_t launch_grouped_gemm(const uint8_t* a_q, const float* a_s, int64_t M_total,
                                const int32_t* off, int G, const uint8_t* w_q, const float* w_s,
                                int64_t N, int64_t K, void* c, int out_bf16, int precise,
@@ -169,7 +169,7 @@ static bool gemm_extent_ok(int64_t rows, int64_t K) {
 
 static fp8q_status gemm_call(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
                              const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
-                             fp8q_out_dtype out, int precise, hipStream_t stream) {
+                             fp8q_out_dtype out, int mode, hipStream_t stream) {
   const bool empty_out = (M == 0 || N == 0);
   const bool empty_k = (K == 0);
   if (!empty_out && !c) return FP8Q_ERR_NULL;
@@ -185,7 +185,7 @@ static fp8q_status gemm_call(const uint8_t* a_q, const float* a_s, const uint8_t
   const fp8q_status d = check_device();
   if (d != FP8Q_OK) return d;
   return launched(
-      fp8q::launch_gemm(a_q, a_s, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16, precise, stream));
+      fp8q::launch_gemm(a_q, a_s, w_q, w_s, M, N, K, c, out == FP8Q_OUT_BF16, mode, stream));
 }
 
 fp8q_status fp8q_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
@@ -198,6 +198,12 @@ fp8q_status fp8q_gemm_precise(const uint8_t* a_q, const float* a_s, const uint8_
                               const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
                               fp8q_out_dtype out, hipStream_t stream) {
   return gemm_call(a_q, a_s, w_q, w_s, M, N, K, c, out, 1, stream);
+}
+
+fp8q_status fp8q_gemm_mfma_scaled(const uint8_t* a_q, const float* a_s, const uint8_t* w_q,
+                                  const float* w_s, int64_t M, int64_t N, int64_t K, void* c,
+                                  fp8q_out_dtype out, hipStream_t stream) {
+  return gemm_call(a_q, a_s, w_q, w_s, M, N, K, c, out, 2, stream);
 }
 
 static fp8q_status grouped_call(const uint8_t* a_q, const float* a_s, int64_t M_total,

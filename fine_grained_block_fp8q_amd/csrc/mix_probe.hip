@@ -20,6 +20,9 @@
 //   kWiden  (FP16 mode, with kReads) the 12 code words read are widened to
 //           FP16 by 24 v_cvt_scalef32_pk_f16_fp8, 1.5 per FP16 MFMA as in the
 //           precise GEMM, each read's words one step after the read.
+//   kScaled (FP8 mode) the MFMAs take E8M0 operand scales from registers
+//           (byte 127 = 1.0 on both operands): the block-scaled form that
+//           fp8q_gemm_mfma_scaled issues.
 // The result of every lane is stored, so nothing is dead code.
 
 #include <hip/hip_runtime.h>
@@ -33,7 +36,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int kReads = 1, kPromote = 2, kWiden = 4, kFp16 = 8;
+constexpr int kReads = 1, kPromote = 2, kWiden = 4, kFp16 = 8, kScaled = 16;
 constexpr int kLdsBytes = 96 * 1024;   // > 80 KiB: one workgroup per CU
 constexpr int kWindow = 64 * 1024;     // the reads cycle through 64 KiB
 
@@ -70,6 +73,8 @@ __global__ __launch_bounds__(512) void mix_kernel(float* __restrict__ out, int i
     p[j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
   const float s = 1.0f + (float)lane * 1e-7f;
+  // E8M0 1.0 in every byte, from memory so the compiler keeps the scaled form
+  const int one = 0x7f7f7f7f ^ (int)(reinterpret_cast<const uint32_t*>(lds)[0] & 0u);
   v4i r0 = rd16(lds, base), r1 = rd16(lds, base + 1024), r2 = rd16(lds, base + 2048);
   v8i a = v8i{r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
   v8i b = v8i{r2[0], r2[1], r2[2], r2[3], r0[0], r0[1], r0[2], r0[3]};
@@ -105,6 +110,9 @@ __global__ __launch_bounds__(512) void mix_kernel(float* __restrict__ out, int i
                                                     __builtin_bit_cast(v8h, qb), c, 0, 0, 0);
         }
         pn[j] = c;
+      } else if constexpr (KIND & kScaled) {
+        pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            j & 1 ? b : a, j & 2 ? a : b, c0, 0, 0, 0, one, 1, one);
       } else {
         pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             j & 1 ? b : a, j & 2 ? a : b, c0, 0, 0, 0, 0, 0, 0);
@@ -167,7 +175,8 @@ void launch(float* out, int blocks, int iters, hipStream_t stream) {
 extern "C" {
 
 // Runs the mix `kind` (a combination of 1 = reads, 2 = promotion, 4 = widening,
-// 8 = FP16 mode; widening needs reads and the FP16 mode) on one workgroup of
+// 8 = FP16 mode, 16 = E8M0-scaled FP8 MFMAs; widening needs reads and the FP16
+// mode) on one workgroup of
 // 8 waves per CU of the current device, each wave `iters` iterations.
 // out: device float[cus * 512].  Returns 0, -1 for an unsupported kind or
 // bad arguments, or the HIP error code.  Asynchronous on `stream`.
@@ -182,6 +191,8 @@ int fp8q_probe_mix(int kind, int iters, float* out, hipStream_t stream) {
     case 1: launch<1>(out, cus, iters, stream); break;
     case 2: launch<2>(out, cus, iters, stream); break;
     case 3: launch<3>(out, cus, iters, stream); break;
+    case 16: launch<16>(out, cus, iters, stream); break;
+    case 19: launch<19>(out, cus, iters, stream); break;
     case 8: launch<8>(out, cus, iters, stream); break;
     case 9: launch<9>(out, cus, iters, stream); break;
     case 10: launch<10>(out, cus, iters, stream); break;

@@ -31,6 +31,7 @@ def _load(path):
     L.fp8q_quantize_weight.argtypes = [p, i64, i64, p, p, i32, p]
     L.fp8q_gemm.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_gemm_precise.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
+    L.fp8q_gemm_mfma_scaled.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
     L.fp8q_grouped_gemm.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
     L.fp8q_grouped_gemm_precise.argtypes = [p, p, i64, p, i32, p, p, i64, i64, p, i32, p]
     L.fp8q_gemm_rowscaled_precise.argtypes = [p, p, p, p, i64, i64, i64, p, i32, p]
@@ -62,7 +63,8 @@ def _no_device():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"fp8q_quantize_act", "fp8q_quantize_weight", "fp8q_gemm",
-                          "fp8q_gemm_precise", "fp8q_grouped_gemm", "fp8q_grouped_gemm_precise",
+                          "fp8q_gemm_precise", "fp8q_gemm_mfma_scaled", "fp8q_grouped_gemm",
+                          "fp8q_grouped_gemm_precise",
                           "fp8q_gemm_bf16", "fp8q_quantize_act_t", "fp8q_quantize_weight_t",
                           "fp8q_gemm_rowscaled", "fp8q_gemm_rowscaled_precise", "fp8q_gemm_fused",
                           "fp8q_grouped_gemm_fused", "fp8q_status_string", "fp8q_abi_version",
@@ -72,7 +74,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fp8q_abi_version() == 2
+    assert lib.fp8q_abi_version() == 3
     assert lib.fp8q_debug_checks() in (0, 1)
     for s in range(9):
         txt = lib.fp8q_status_string(s).decode()
@@ -114,7 +116,7 @@ def test_debug_checks_flag():
     assert _load(LIB_DEBUG).fp8q_debug_checks() == 1
 
 
-@pytest.mark.parametrize("name", ["fp8q_gemm", "fp8q_gemm_precise"])
+@pytest.mark.parametrize("name", ["fp8q_gemm", "fp8q_gemm_precise", "fp8q_gemm_mfma_scaled"])
 def test_gemm_validation(lib, name):
     f = getattr(lib, name)
     assert f(A, A, A, A, 4, 128, 128, None, 0, None) == E_NULL
@@ -250,6 +252,7 @@ def test_valid_arguments_without_gpu_report_device_error(lib):
     assert lib.fp8q_gemm_fused(A, A, A, 4, 128, 128, A, 0, 1, None) == E_DEVICE
     assert lib.fp8q_grouped_gemm_fused(A, 8, A, 2, A, A, 128, 128, A, 0, 0, None) == E_DEVICE
     assert lib.fp8q_gemm_precise(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
+    assert lib.fp8q_gemm_mfma_scaled(A, A, A, A, 4, 128, 128, A, 1, None) == E_DEVICE
     assert lib.fp8q_grouped_gemm_precise(A, A, 8, A, 2, A, A, 128, 128, A, 0, None) == E_DEVICE
     assert lib.fp8q_gemm_rowscaled_precise(A, A, A, A, 4, 128, 128, A, 0, None) == E_DEVICE
 
