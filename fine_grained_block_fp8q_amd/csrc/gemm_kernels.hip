@@ -39,9 +39,12 @@
 // FP8 path, accumulating in the matrix core); the precise mode (OP =
 // kOpWide16: the E4M3 codes, unchanged in LDS, are widened exactly to FP16 in
 // registers and each chunk's partial is formed by FP16 MFMAs, whose FP32
-// accumulation has no narrow truncation step); BF16 activations quantized on
-// their way into LDS (A_CAST, see ACaster); and the grouped MoE kernel's
-// row-count buckets (persistent workgroups, see grouped_gemm_kernel).
+// accumulation has no narrow truncation step); power-of-two scales applied by
+// the matrix core as E8M0 operand scales (OP = kOpFp8Mx, the pages' "MMA with
+// group scaling" wish: the partial comes out scaled and the promotion is an
+// add); BF16 activations quantized on their way into LDS (A_CAST, see
+// ACaster); and the grouped MoE kernel's row-count buckets (persistent
+// workgroups, see grouped_gemm_kernel).
 
 #include <type_traits>
 
