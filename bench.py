@@ -228,16 +228,23 @@ def mix_probe(iters=20000, rounds=5):
 
 RING_SHAPES = [  # (activation rows per tile, ring stages): the grouped GEMM's tiles
     (0, 2), (0, 3), (0, 4), (64, 3), (128, 3), (160, 3), (192, 2), (256, 2)]
+RING_SPLIT_SHAPES = [  # (activation rows, activation stages, weight stages): split rings
+    (64, 2, 4), (128, 2, 3), (128, 2, 4), (128, 3, 3), (192, 2, 2), (192, 2, 3), (256, 2, 2),
+    (256, 2, 3)]
 
 
 def ring_probe(rounds=5):
     """The ring-streaming probe of libfp8q_probe.so: one workgroup per CU
     streams tiles of 256 weight rows of its own plus `ra` activation rows
     shared by the 16 tiles of an expert, K = 7168, through an LDS ring of
-    `stages` stages, with no MFMA.  Two regimes: 16 tiles per CU (7.5 GB of
-    weights, the MoE batch's volume) and 2 tiles per CU (0.94 GB, the decode
-    batch's).  Median over `rounds` launches (HIP events); weight GB/s counts
-    the weight bytes, total GB/s adds the activation bytes each tile reads."""
+    `stages` stages, with no MFMA; then the split variant, whose activation
+    rows and weight rows have rings of their own depths (`a_stages`,
+    `w_stages`).  Regimes: 16 tiles per CU (7.5 GB of weights, the MoE
+    batch's volume) and 2 tiles per CU (0.94 GB, the decode batch's), and an
+    L2-resident one (all tiles read the same weight rows).  Median over
+    `rounds` launches (HIP events); weight GB/s counts the weight bytes, total
+    GB/s adds the activation bytes each tile reads.  Ends with the decode and
+    MoE ceilings these rates give (ring_ceilings)."""
     import ctypes
     import torch
     L = _probe_lib()
@@ -245,6 +252,11 @@ def ring_probe(rounds=5):
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     L.fp8q_probe_ring.restype = ctypes.c_int
+    L.fp8q_probe_ring_split.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p]
+    L.fp8q_probe_ring_split.restype = ctypes.c_int
     L.fp8q_probe_cus.restype = ctypes.c_int
     cus = L.fp8q_probe_cus()
     K, per_expert = 7168, 16
@@ -254,17 +266,30 @@ def ring_probe(rounds=5):
     a.fill_(0x38)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     rows = []
-    for tiles in (16, 2):
-        w_rows = cus * tiles * 256
-        for ra, stages in RING_SHAPES:
-            a_rows = 256 * ra if ra else 0
+    shapes = [(ra, s, s, False) for ra, s in RING_SHAPES] + \
+        [(ra, sa, sw, True) for ra, sa, sw in RING_SPLIT_SHAPES]
+    # Regimes: weights from HBM at the MoE and decode volumes, and a check of
+    # the CU side, where every tile reads the same 256 weight rows and one
+    # expert's activation rows, so that after the first touch both hit in L2.
+    regimes = [(16, "hbm", shapes), (2, "hbm", shapes),
+               (16, "l2", [x for x in shapes if not x[3] and x[0] in (0, 128, 256)])]
+    for tiles, src, rshapes in regimes:
+        w_rows = cus * tiles * 256 if src == "hbm" else 256
+        for ra, a_st, stages, split in rshapes:
+            a_rows = (256 * ra if src == "hbm" else ra) if ra else 0
 
             def run():
-                st = L.fp8q_probe_ring(ctypes.c_void_p(w.data_ptr()), w_rows,
-                                       ctypes.c_void_p(a.data_ptr()), a_rows, K, ra, stages,
-                                       tiles, per_expert, stream)
+                if split:
+                    st = L.fp8q_probe_ring_split(ctypes.c_void_p(w.data_ptr()), w_rows,
+                                                 ctypes.c_void_p(a.data_ptr()), a_rows, K, ra,
+                                                 a_st, stages, tiles, per_expert, stream)
+                else:
+                    st = L.fp8q_probe_ring(ctypes.c_void_p(w.data_ptr()), w_rows,
+                                           ctypes.c_void_p(a.data_ptr()), a_rows, K, ra, stages,
+                                           tiles, per_expert, stream)
                 if st != 0:
-                    raise RuntimeError(f"fp8q_probe_ring({ra}, {stages}) failed: {st}")
+                    raise RuntimeError(f"ring probe ({ra}, {a_st}, {stages}, split={split}) "
+                                       f"failed: {st}")
 
             run()
             ts = []
@@ -278,10 +303,56 @@ def ring_probe(rounds=5):
             us = float(np.median(ts))
             wb = cus * tiles * 256 * K
             ab = cus * tiles * ra * K
-            rows.append({"tiles_per_cu": tiles, "act_rows": ra, "stages": stages, "us": us,
+            rows.append({"tiles_per_cu": tiles, "weights": src, "act_rows": ra, "split": split,
+                         "act_stages": a_st, "stages": stages, "us": us,
                          "weight_GB_s": wb / us / 1e3, "total_GB_s": (wb + ab) / us / 1e3})
+            print(json.dumps(rows[-1]), flush=True)
     print(json.dumps({"ring_probe": rows, "K": K, "weight_rows_per_tile": 256,
-                      "tiles_per_expert": per_expert, "workgroups": cus, "rounds": rounds}))
+                      "tiles_per_expert": per_expert, "workgroups": cus, "rounds": rounds,
+                      "ceilings": ring_ceilings(rows)}))
+
+
+# The grouped GEMM's row buckets (tile rows <= bucket) with their ring depths.
+GROUPED_BUCKETS = [(64, 3), (128, 3), (160, 3), (192, 2), (256, 2)]
+
+
+def ring_ceilings(rows):
+    """Streaming ceiling of the decode and MoE workloads from the ring probe's
+    rates: every m-tile of an expert (at most 256 rows) runs N/256 tiles in its
+    row bucket's ring, each streaming 256 x K weight bytes at that bucket's
+    measured weight rate (2 tiles per CU for decode, 16 for MoE, as the two
+    batches load the chip); the tiles' times add up.  The output writes are
+    left out, so the ceiling is optimistic.  GB/s = algorithmic bytes / time."""
+    import workloads
+    out = {}
+    for name, tiles_per_cu in (("decode", 2), ("moe", 16)):
+        c = workloads.WORKLOADS[name]
+        N, K = c["N"], c["K"]
+        if name == "moe":
+            counts, _, _ = workloads.moe_routing(c["tokens"], c["experts"], c["topk"], c["seed"])
+            ob = 4
+        else:
+            counts, _ = workloads.decode_counts(c["experts"], c["m_lo"], c["m_hi"], c["seed"])
+            ob = 2
+        rate = {ra: r["weight_GB_s"] for r in rows for ra, st in GROUPED_BUCKETS
+                if not r["split"] and r["tiles_per_cu"] == tiles_per_cu
+                and r.get("weights", "hbm") == "hbm"
+                and r["act_rows"] == ra and r["stages"] == st}
+        t_us, per_bucket = 0.0, {}
+        for m in counts:
+            m = int(m)
+            while m > 0:
+                live = min(m, 256)
+                b = next(ra for ra, _ in GROUPED_BUCKETS if live <= ra)
+                per_bucket[b] = per_bucket.get(b, 0) + 1
+                t_us += (N // 256) * 256 * K / (rate[b] * 1e3)
+                m -= live
+        G, Mt = len(counts), int(counts.sum())
+        gbytes = G * N * K * (1 + 4 / 16384) + Mt * K * (1 + 4 / 128) + Mt * N * ob
+        out[name] = {"us": t_us, "GB_s": gbytes / t_us / 1e3,
+                     "frac_hbm": gbytes / t_us / 1e3 / PEAK_HBM_GBS,
+                     "m_tiles_per_bucket": {str(k): v for k, v in sorted(per_bucket.items())}}
+    return out
 
 
 def gemm_bytes(M, N, K, out_bytes):

@@ -269,8 +269,18 @@ def test_probe_library_exports_and_validation():
     L.fp8q_probe_mix.argtypes = [ctypes.c_int, ctypes.c_int, p, p]
     L.fp8q_probe_ring.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, p]
-    for name in ("fp8q_probe_stream", "fp8q_probe_mix", "fp8q_probe_cus", "fp8q_probe_ring"):
+    L.fp8q_probe_ring_split.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, p]
+    for name in ("fp8q_probe_stream", "fp8q_probe_mix", "fp8q_probe_cus", "fp8q_probe_ring",
+                 "fp8q_probe_ring_split"):
         assert hasattr(L, name)
+    split = L.fp8q_probe_ring_split
+    assert split(p(4096), 256, None, 256, 7168, 256, 2, 3, 1, 16, None) == -1     # no A
+    assert split(p(4096), 256, p(8192), 256, 7168, 0, 2, 3, 1, 16, None) == -1    # ra = 0
+    assert split(p(4096), 256, p(8192), 300, 7168, 256, 2, 3, 1, 16, None) == -1  # a_rows
+    assert split(p(4096), 256, p(8192), 256, 7168, 256, 3, 3, 1, 16, None) == -1  # no such ring
+    assert split(p(4096), 256, p(8192), 256, 7100, 256, 2, 3, 1, 16, None) == -1  # K
     assert L.fp8q_probe_ring(None, 256, None, 0, 7168, 0, 2, 1, 16, None) == -1
     assert L.fp8q_probe_ring(p(4096), 100, None, 0, 7168, 0, 2, 1, 16, None) == -1   # w_rows
     assert L.fp8q_probe_ring(p(4096), 256, None, 128, 7168, 128, 3, 1, 16, None) == -1  # no A
