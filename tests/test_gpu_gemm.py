@@ -177,6 +177,28 @@ def _check_grouped(c, A, Wst, off, experts, out="f32", max_rows=None, precise=Fa
                                 what=f"expert {e}")
 
 
+def _assert_every_expert_equals_dense(c, cp, aq, as_, off, wq, ws, what):
+    """Every row of a full-size grouped output, fast (c) and precise (cp), is
+    bitwise equal to the dense GEMM of its expert's weights on that expert's
+    rows: an output's arithmetic does not depend on the tile that computes it
+    (one chunk partial per MFMA block, the same promotion order), so this
+    carries the dense path's oracle checks to every output of the workload."""
+    f = fq()
+    bits = (lambda t: t.view(torch.int16)) if c.dtype == torch.bfloat16 else \
+        (lambda t: t.view(torch.int32))
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        a_e, s_e = aq[lo:hi].contiguous(), as_[:, lo:hi].contiguous()
+        ce = f.gemm(a_e, s_e, wq[e], ws[e], out_dtype=c.dtype)
+        cpe = f.gemm(a_e, s_e, wq[e], ws[e], out_dtype=c.dtype, precise=True)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(c[lo:hi]), bits(ce)), f"{what}: expert {e} differs from dense"
+        assert torch.equal(bits(cp[lo:hi]), bits(cpe)), \
+            f"{what}: precise expert {e} differs from dense"
+
+
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("precise", [False, True])
 def test_grouped_small_with_empty_experts(out, precise):
@@ -198,7 +220,8 @@ def test_grouped_single_expert_equals_dense(precise):
 
 def test_grouped_decode_workload_sampled():
     """Decode shape: 32 experts, M_e uniform in [16, 256], N 4096, K 7168, BF16
-    out; expert weights drawn on the device, oracle on 4 sampled experts."""
+    out; expert weights drawn on the device, oracle on 4 sampled experts, and
+    every expert's rows bitwise equal to the dense GEMM on them."""
     cfg = workloads.WORKLOADS["decode"]
     counts, off = workloads.decode_counts(cfg["experts"], cfg["m_lo"], cfg["m_hi"], cfg["seed"])
     G, N, K = cfg["experts"], cfg["N"], cfg["K"]
@@ -231,6 +254,7 @@ def test_grouped_decode_workload_sampled():
                             bound_cols=cols, what=f"decode expert {e}")
         assert_gemm_strict(chp[rows], qa[rows], sa[:, rows], qw, sw, out="bf16",
                            what=f"decode precise expert {e}")
+    _assert_every_expert_equals_dense(c, cp, aq, as_, off, args[3], args[4], "decode")
 
 
 @pytest.mark.parametrize("precise", [False, True])
@@ -256,7 +280,8 @@ def test_grouped_moe_workload_sampled():
     (32768 gathered rows), N 4096, K 7168, FP32 out, in the launch bench.py
     times.  Weights are drawn on the device and quantized expert by expert;
     the oracle checks the codes of 4 sampled experts bit-exactly and their
-    GEMM outputs on sampled rows, plus the activation codes of those rows."""
+    GEMM outputs on sampled rows, plus the activation codes of those rows;
+    every expert's rows are bitwise equal to the dense GEMM on them."""
     cfg = workloads.WORKLOADS["moe"]
     G, N, K = cfg["experts"], cfg["N"], cfg["K"]
     counts, off, token_of = workloads.moe_routing(cfg["tokens"], G, cfg["topk"], cfg["seed"])
@@ -295,6 +320,7 @@ def test_grouped_moe_workload_sampled():
         assert_gemm_bounded(ch, qa, sa, qw, sw, bound_cols=cols, what=f"moe expert {e}")
         chp = host(cp[torch.from_numpy(rows).to(DEV)])
         assert_gemm_strict(chp, qa, sa, qw, sw, what=f"moe precise expert {e}")
+    _assert_every_expert_equals_dense(c, cp, aq, as_, off, wq, ws, "moe")
 
 
 @pytest.mark.parametrize("G", [1000, 1024])
