@@ -102,7 +102,8 @@ def assert_gemm_bounded(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=Fal
     return res
 
 
-def assert_gemm_strict(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=False):
+def assert_gemm_strict(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=False, ref=None,
+                       absb=None):
     """Acceptance of the precise GEMMs, on EVERY output:
 
     1. the stated tolerance |C_gpu - C_exact| <= 1e-5 * sum_k |dec(a_k) s_a|
@@ -115,13 +116,16 @@ def assert_gemm_strict(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=Fals
     C_exact from the exact oracle (oracle.gemm).  c_gpu: numpy [M][N]
     (float32, or BF16 widened); operands qa [M][K], sa [K/128][M], qw [N][K],
     sw [N/128][K/128] (rowscaled: sw is [K/128][N] row-group scales).
+    ref / absb: oracle.gemm and oracle.abs_bound of these operands, when the
+    caller has them already (full-size checks share them between calls).
     Returns statistics."""
-    if rowscaled:
-        ref = ogemm.gemm_rowscaled(qa, sa, qw, sw)
-        absb = ogemm.abs_bound_rowscaled(qa, sa, qw, sw)
-    else:
-        ref = ogemm.gemm(qa, sa, qw, sw)
-        absb = ogemm.abs_bound(qa, sa, qw, sw)
+    if ref is None or absb is None:
+        if rowscaled:
+            ref = ogemm.gemm_rowscaled(qa, sa, qw, sw)
+            absb = ogemm.abs_bound_rowscaled(qa, sa, qw, sw)
+        else:
+            ref = ogemm.gemm(qa, sa, qw, sw)
+            absb = ogemm.abs_bound(qa, sa, qw, sw)
     G = qa.shape[1] // 128
     half = ogemm.bf16_half_ulp(ref) if out == "bf16" else 0.0
     tol = 1e-5 * absb + half
