@@ -34,7 +34,10 @@ Modules:
   gemm        block-scaled GEMM with per-128-K promotion, exact in float64; the
               variant with row-group scales on both operands (weight gradient);
               the BF16 reference product
-  mfma_model  model of the gfx950 FP8 matrix core's dot product (parity tier 1)
+  mfma_model  model of the gfx950 FP8 matrix core's dot product (a diagnostic)
+              and the truncation term T of the fast GEMM's a-priori bound, also
+              evaluated by a plain C loop (truncation_bound.c) for full-size
+              matrices
   narrow_acc  emulator of a narrow fixed-point accumulator (accuracy study)
 """
 

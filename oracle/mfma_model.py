@@ -158,6 +158,36 @@ def truncation_bound(qa, sa, qw, sw, rowscaled=False):
     return out
 
 
+def truncation_bound_native(qa, sa, qw, sw):
+    """truncation_bound for block-scaled operands, evaluated by the plain C
+    loop of oracle/truncation_bound.c (oracle/libtbound.so, built by
+    __graft_entry__.build()) for full-size matrices; bit-identical to
+    truncation_bound (every chunk's sum of lost terms is exact in double)."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtbound.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built (__graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    fn = lib.fp8q_oracle_truncation_bound
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    fn.restype = None
+    qa = np.ascontiguousarray(qa, dtype=np.uint8)
+    qw = np.ascontiguousarray(qw, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    M, K = qa.shape
+    N = qw.shape[0]
+    if (qw.shape[1] != K or K % GROUP or N % GROUP or sa.shape != (K // GROUP, M)
+            or sw.shape != (N // GROUP, K // GROUP)):
+        raise ValueError("truncation_bound_native: operand shapes do not match")
+    out = np.empty((M, N), dtype=np.float64)
+    fn(qa.ctypes.data, sa.ctypes.data, qw.ctypes.data, sw.ctypes.data, M, N, K,
+       out.ctypes.data)
+    return out
+
+
 def fp32_rounding_bound(qa, sa, qw, sw, abs_bound):
     """Bound on |C_gpu - C_model| from FP32 rounding alone.
 

@@ -31,7 +31,8 @@ def host(t):
 
 
 def assert_gemm_bounded(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=False,
-                        bound_cols=None, model_rows=0, seed=0):
+                        bound_cols=None, model_rows=0, seed=0, ref=None, absb=None,
+                        native=False):
     """Acceptance of the FP8-MFMA GEMMs (fp8q_gemm and the calls sharing its
     arithmetic): on every checked output
 
@@ -51,14 +52,19 @@ def assert_gemm_bounded(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=Fal
     fraction of outputs within the stated 1e-5 * sum|a||b| tolerance and, on
     ``model_rows`` random rows, the largest deviation from oracle.mfma_model
     in units of its FP32 rounding bound (reported, not asserted).
+    ref / absb: oracle.gemm and oracle.abs_bound of these operands, when the
+    caller has them already.  native: T from the oracle's C evaluation
+    (mfma_model.truncation_bound_native, block-scaled operands), for bounds
+    over whole full-size outputs.
     """
     from oracle import mfma_model
-    if rowscaled:
-        ref = ogemm.gemm_rowscaled(qa, sa, qw, sw)
-        absb = ogemm.abs_bound_rowscaled(qa, sa, qw, sw)
-    else:
-        ref = ogemm.gemm(qa, sa, qw, sw)
-        absb = ogemm.abs_bound(qa, sa, qw, sw)
+    if ref is None or absb is None:
+        if rowscaled:
+            ref = ogemm.gemm_rowscaled(qa, sa, qw, sw)
+            absb = ogemm.abs_bound_rowscaled(qa, sa, qw, sw)
+        else:
+            ref = ogemm.gemm(qa, sa, qw, sw)
+            absb = ogemm.abs_bound(qa, sa, qw, sw)
     M, K = qa.shape
     G = K // 128
     err = np.abs(c_gpu.astype(np.float64) - ref)
@@ -74,7 +80,11 @@ def assert_gemm_bounded(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=Fal
         assert len(cols) % 128 == 0 and np.all(cols.reshape(-1, 128) // 128 ==
                                                (cols.reshape(-1, 128) // 128)[:, :1])
         sw_c = sw[cols[::128] // 128]
-    T = mfma_model.truncation_bound(qa, sa, qw[cols], sw_c, rowscaled)
+    if native:
+        assert not rowscaled, "the C evaluation covers block-scaled operands"
+        T = mfma_model.truncation_bound_native(qa, sa, qw[cols], sw_c)
+    else:
+        T = mfma_model.truncation_bound(qa, sa, qw[cols], sw_c, rowscaled)
     fp32 = (G + 20) * mfma_model.U32 * absb[:, cols]
     half_c = half[:, cols] if out == "bf16" else 0.0
     lim = T + fp32 + half_c
