@@ -29,8 +29,8 @@ rotated so that every step streams its inputs from HBM rather than from the
 256 MiB last-level cache.  Per-kernel durations come from HIP events recorded
 on the stream the kernels are launched on (torch's current stream).
 
-Prints ONE JSON line (rank 0).  ``--gpus`` above 1 is refused: this build runs
-on one GPU.
+Prints ONE JSON line (rank 0).  ``--gpus`` above 1 is refused: the benchmark
+measures one GPU.
 """
 
 import argparse
@@ -842,7 +842,7 @@ def main():
         print(json.dumps({"error": "--mfma-scaled applies to the dense and largek workloads only"}))
         sys.exit(2)
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark measures one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)

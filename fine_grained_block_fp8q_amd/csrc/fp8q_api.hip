@@ -124,7 +124,7 @@ const char* fp8q_status_string(fp8q_status st) {
     case FP8Q_ERR_ENUM: return "FP8Q_ERR_ENUM: unknown scale mode or output dtype";
     case FP8Q_ERR_DEVICE: return "FP8Q_ERR_DEVICE: no current HIP device, or it is not gfx950";
     case FP8Q_ERR_LAUNCH: return "FP8Q_ERR_LAUNCH: kernel launch failed";
-    case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: not implemented in this build";
+    case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: valid request outside what the library implements";
     case FP8Q_ERR_OFFSETS:
       return "FP8Q_ERR_OFFSETS: device offsets not 0 = off[0] <= ... <= off[G] <= M_total "
              "(reported by FP8Q_DEBUG_CHECKS builds)";

@@ -62,7 +62,7 @@ typedef enum {
   FP8Q_ERR_ENUM = 4,        /* unknown scale mode or output dtype              */
   FP8Q_ERR_DEVICE = 5,      /* no current HIP device, or it is not gfx950      */
   FP8Q_ERR_LAUNCH = 6,      /* the kernel launch failed                        */
-  FP8Q_ERR_UNSUPPORTED = 7, /* valid request this build does not implement     */
+  FP8Q_ERR_UNSUPPORTED = 7, /* valid request the library does not implement   */
   FP8Q_ERR_OFFSETS = 8      /* grouped calls, FP8Q_DEBUG_CHECKS builds only: the
                                device offsets are not 0 = off[0] <= ... <=
                                off[G] <= M_total                                  */
