@@ -228,6 +228,8 @@ def mix_probe(iters=20000, rounds=5):
 
 RING_SHAPES = [  # (activation rows per tile, ring stages): the grouped GEMM's tiles
     (0, 2), (0, 3), (0, 4), (64, 3), (128, 3), (160, 3), (192, 2), (256, 2)]
+RING_READ_SHAPES = [  # (activation rows, stages, LDS reads per wave and chunk)
+    (0, 2, 24), (128, 3, 12), (128, 3, 24), (256, 2, 24)]
 RING_SPLIT_SHAPES = [  # (activation rows, activation stages, weight stages): split rings
     (64, 2, 4), (128, 2, 3), (128, 2, 4), (128, 3, 3), (192, 2, 2), (192, 2, 3), (256, 2, 2),
     (256, 2, 3)]
@@ -257,6 +259,8 @@ def ring_probe(rounds=5):
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_void_p]
     L.fp8q_probe_ring_split.restype = ctypes.c_int
+    L.fp8q_probe_ring_reads.argtypes = L.fp8q_probe_ring_split.argtypes
+    L.fp8q_probe_ring_reads.restype = ctypes.c_int
     L.fp8q_probe_cus.restype = ctypes.c_int
     cus = L.fp8q_probe_cus()
     K, per_expert = 7168, 16
@@ -266,20 +270,27 @@ def ring_probe(rounds=5):
     a.fill_(0x38)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     rows = []
-    shapes = [(ra, s, s, False) for ra, s in RING_SHAPES] + \
-        [(ra, sa, sw, True) for ra, sa, sw in RING_SPLIT_SHAPES]
+    # (act rows, act stages, stages, variant): variant 0 the kernel's ring, 1
+    # split rings, or ("reads", n) the kernel's ring with n LDS reads per wave
+    shapes = [(ra, s, s, 0) for ra, s in RING_SHAPES] + \
+        [(ra, sa, sw, 1) for ra, sa, sw in RING_SPLIT_SHAPES] + \
+        [(ra, s, s, ("reads", rd)) for ra, s, rd in RING_READ_SHAPES]
     # Regimes: weights from HBM at the MoE and decode volumes, and a check of
     # the CU side, where every tile reads the same 256 weight rows and one
     # expert's activation rows, so that after the first touch both hit in L2.
     regimes = [(16, "hbm", shapes), (2, "hbm", shapes),
-               (16, "l2", [x for x in shapes if not x[3] and x[0] in (0, 128, 256)])]
+               (16, "l2", [x for x in shapes if x[3] == 0 and x[0] in (0, 128, 256)])]
     for tiles, src, rshapes in regimes:
         w_rows = cus * tiles * 256 if src == "hbm" else 256
         for ra, a_st, stages, split in rshapes:
             a_rows = (256 * ra if src == "hbm" else ra) if ra else 0
 
             def run():
-                if split:
+                if isinstance(split, tuple):
+                    st = L.fp8q_probe_ring_reads(ctypes.c_void_p(w.data_ptr()), w_rows,
+                                                 ctypes.c_void_p(a.data_ptr()), a_rows, K, ra,
+                                                 stages, split[1], tiles, per_expert, stream)
+                elif split:
                     st = L.fp8q_probe_ring_split(ctypes.c_void_p(w.data_ptr()), w_rows,
                                                  ctypes.c_void_p(a.data_ptr()), a_rows, K, ra,
                                                  a_st, stages, tiles, per_expert, stream)
@@ -303,7 +314,9 @@ def ring_probe(rounds=5):
             us = float(np.median(ts))
             wb = cus * tiles * 256 * K
             ab = cus * tiles * ra * K
-            rows.append({"tiles_per_cu": tiles, "weights": src, "act_rows": ra, "split": split,
+            rows.append({"tiles_per_cu": tiles, "weights": src, "act_rows": ra,
+                         "split": split == 1,
+                         "lds_reads": split[1] if isinstance(split, tuple) else 0,
                          "act_stages": a_st, "stages": stages, "us": us,
                          "weight_GB_s": wb / us / 1e3, "total_GB_s": (wb + ab) / us / 1e3})
             print(json.dumps(rows[-1]), flush=True)
@@ -336,7 +349,7 @@ def ring_ceilings(rows):
             ob = 2
         rate = {ra: r["weight_GB_s"] for r in rows for ra, st in GROUPED_BUCKETS
                 if not r["split"] and r["tiles_per_cu"] == tiles_per_cu
-                and r.get("weights", "hbm") == "hbm"
+                and r.get("weights", "hbm") == "hbm" and not r.get("lds_reads", 0)
                 and r["act_rows"] == ra and r["stages"] == st}
         t_us, per_bucket = 0.0, {}
         for m in counts:

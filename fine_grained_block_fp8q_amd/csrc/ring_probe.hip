@@ -19,6 +19,14 @@
 // reads: what it measures is the streaming ceiling of the tile shape, S - 1
 // chunks in flight per CU.
 //
+// The reads variant adds, after each chunk's barrier, RD 16-byte LDS reads
+// per lane of every wave from the stage of the chunk that just landed (1 KiB
+// per instruction, consumed into a running XOR), the GEMM main loop's
+// fragment-read volume with no MFMA: it measures how LDS reads slow the
+// direct-to-LDS stream beside them.  (The reads race with the loads refilling
+// other stages and with the next refill of their own; their values are
+// never used.)
+//
 // The split variant gives the activation rows a ring of SA stages and the
 // weight rows one of SW >= SA stages: per chunk every wave issues its loads
 // of activation chunk g + SA - 1, then of weight chunk g + SW - 1 (the same
@@ -37,6 +45,7 @@ namespace fp8q_ring_probe {
 
 using fp8q::make_rsrc;
 using fp8q::to_lds;
+using fp8q::v4i;
 using fp8q::wait_vmcnt;
 
 constexpr int kWRows = 256;
@@ -80,16 +89,17 @@ __device__ __forceinline__ int64_t tile_of(int i, int tiles_per_wg) {
   return ((int64_t)xcd * tiles_per_wg + i) * per_xcd + slot;
 }
 
-template <int RA, int S>
+template <int RA, int S, int RD = 0>
 __global__ __launch_bounds__(512) void ring_kernel(const uint8_t* __restrict__ W, int64_t w_rows,
                                                    const uint8_t* __restrict__ A, int64_t a_rows,
                                                    int64_t K, int tiles_per_wg,
-                                                   int tiles_per_expert) {
+                                                   int tiles_per_expert, int* __restrict__ sink) {
   using R = Ring<RA, S>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[R::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t G = K / 128;
+  v4i seen = v4i{0, 0, 0, 0};
   for (int i = 0; i < tiles_per_wg; ++i) {
     const int64_t tile = tile_of(i, tiles_per_wg);
     const int64_t w0 = (tile * kWRows) % w_rows;
@@ -116,17 +126,28 @@ __global__ __launch_bounds__(512) void ring_kernel(const uint8_t* __restrict__ W
       issue_chunk<RA, S>(lds, ra, rw, voff, dst, is_a, g + S - 1, G);
       wait_vmcnt<R::PER_WAVE * (S - 1)>();  // chunk g landed
       __builtin_amdgcn_s_barrier();
+      if constexpr (RD > 0) {
+        const uint8_t* stage = lds + (int)(g % S) * R::STAGE;
+#pragma unroll
+        for (int r = 0; r < RD; ++r) {
+          const int off = ((wave * RD + r) * 1024 + lane * 16) % R::STAGE;
+          seen ^= *reinterpret_cast<const v4i*>(stage + off);
+        }
+      }
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
   }
+  // Keeps the reads: a store the host never asks for (sink is null).
+  if (sink != nullptr && (seen[0] ^ seen[1] ^ seen[2] ^ seen[3]) == 0x5a5a5a5a)
+    sink[blockIdx.x] = threadIdx.x;
 }
 
-template <int RA, int S>
+template <int RA, int S, int RD = 0>
 hipError_t launch(const uint8_t* W, int64_t w_rows, const uint8_t* A, int64_t a_rows, int64_t K,
                   int blocks, int tiles_per_wg, int tiles_per_expert, hipStream_t stream) {
-  ring_kernel<RA, S><<<dim3(blocks), dim3(512), 0, stream>>>(W, w_rows, A, a_rows, K,
-                                                             tiles_per_wg, tiles_per_expert);
+  ring_kernel<RA, S, RD><<<dim3(blocks), dim3(512), 0, stream>>>(
+      W, w_rows, A, a_rows, K, tiles_per_wg, tiles_per_expert, nullptr);
   return hipGetLastError();
 }
 
@@ -253,6 +274,36 @@ int fp8q_probe_ring(const void* W, int64_t w_rows, const void* A, int64_t a_rows
   else if (ra == 256 && stages == 2) e = launch<256, 2>(w, w_rows, a, a_rows, K, cus, tiles_per_wg, tiles_per_expert, stream);
   else return -1;
   return (int)e;
+}
+
+// The reads variant: the kernel's ring for (ra, stages) as in fp8q_probe_ring,
+// plus `reads` 16-byte LDS reads per lane of every wave per chunk; (ra,
+// stages, reads) one of (0, 2, 24), (128, 3, 12), (128, 3, 24), (256, 2, 24)
+// (24 reads per wave are the 256 x 256 tile's fragment reads per chunk; the
+// 128-row tile's 4 live waves make 12 per wave on average).  Arguments
+// otherwise as for fp8q_probe_ring; returns 0, -1 for unsupported arguments,
+// or the HIP error code.  Asynchronous on `stream`.
+int fp8q_probe_ring_reads(const void* W, int64_t w_rows, const void* A, int64_t a_rows,
+                          int64_t K, int ra, int stages, int reads, int tiles_per_wg,
+                          int tiles_per_expert, hipStream_t stream) {
+  using Launch = hipError_t (*)(const uint8_t*, int64_t, const uint8_t*, int64_t, int64_t, int,
+                                int, int, hipStream_t);
+  Launch f = nullptr;
+  if (ra == 0 && stages == 2 && reads == 24) f = launch<0, 2, 24>;
+  else if (ra == 128 && stages == 3 && reads == 12) f = launch<128, 3, 12>;
+  else if (ra == 128 && stages == 3 && reads == 24) f = launch<128, 3, 24>;
+  else if (ra == 256 && stages == 2 && reads == 24) f = launch<256, 2, 24>;
+  if (!f || !W || w_rows <= 0 || w_rows % kWRows || K <= 0 || K % 128 ||
+      kWRows * K >= (1ll << 31) || tiles_per_wg <= 0 || tiles_per_expert <= 0 ||
+      (ra > 0 && (!A || a_rows < ra || a_rows % ra || (int64_t)ra * K >= (1ll << 31))))
+    return -1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return (int)hipGetLastError();
+  if (cus % 8) return -1;   // the tile hand-out assumes 8 XCDs of equal size
+  return (int)f(static_cast<const uint8_t*>(W), w_rows, static_cast<const uint8_t*>(A), a_rows,
+                K, cus, tiles_per_wg, tiles_per_expert, stream);
 }
 
 // The split-ring variant: ra activation rows in a ring of a_stages stages,

@@ -272,9 +272,14 @@ def test_probe_library_exports_and_validation():
     L.fp8q_probe_ring_split.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, p]
+    L.fp8q_probe_ring_reads.argtypes = L.fp8q_probe_ring_split.argtypes
     for name in ("fp8q_probe_stream", "fp8q_probe_mix", "fp8q_probe_cus", "fp8q_probe_ring",
-                 "fp8q_probe_ring_split"):
+                 "fp8q_probe_ring_split", "fp8q_probe_ring_reads"):
         assert hasattr(L, name)
+    reads = L.fp8q_probe_ring_reads
+    assert reads(p(4096), 256, p(8192), 256, 7168, 256, 2, 7, 1, 16, None) == -1  # no such count
+    assert reads(p(4096), 256, None, 256, 7168, 256, 2, 24, 1, 16, None) == -1    # no A
+    assert reads(p(4096), 100, None, 0, 7168, 0, 2, 24, 1, 16, None) == -1        # w_rows
     split = L.fp8q_probe_ring_split
     assert split(p(4096), 256, None, 256, 7168, 256, 2, 3, 1, 16, None) == -1     # no A
     assert split(p(4096), 256, p(8192), 256, 7168, 0, 2, 3, 1, 16, None) == -1    # ra = 0
