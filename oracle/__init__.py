@@ -38,6 +38,7 @@ Modules:
               and the truncation term T of the fast GEMM's a-priori bound, also
               evaluated by a plain C loop (truncation_bound.c) for full-size
               matrices
+  native      builds and loads that C loop (libtbound.so)
   narrow_acc  emulator of a narrow fixed-point accumulator (accuracy study)
 """
 

@@ -161,15 +161,12 @@ def truncation_bound(qa, sa, qw, sw, rowscaled=False):
 def truncation_bound_native(qa, sa, qw, sw):
     """truncation_bound for block-scaled operands, evaluated by the plain C
     loop of oracle/truncation_bound.c (oracle/libtbound.so, built by
-    __graft_entry__.build()) for full-size matrices; bit-identical to
-    truncation_bound (every chunk's sum of lost terms is exact in double)."""
+    __graft_entry__.build(), or on first use) for full-size matrices;
+    bit-identical to truncation_bound (every chunk's sum of lost terms is
+    exact in double)."""
     import ctypes
-    import os
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtbound.so")
-    if not os.path.exists(path):
-        raise ImportError(f"{path} is not built (__graft_entry__.build())")
-    lib = ctypes.CDLL(path)
-    fn = lib.fp8q_oracle_truncation_bound
+    from . import native
+    fn = native.load().fp8q_oracle_truncation_bound
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     fn.restype = None
