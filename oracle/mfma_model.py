@@ -158,17 +158,17 @@ def truncation_bound(qa, sa, qw, sw, rowscaled=False):
     return out
 
 
-def truncation_bound_native(qa, sa, qw, sw):
-    """truncation_bound for block-scaled operands, evaluated by the plain C
-    loop of oracle/truncation_bound.c (oracle/libtbound.so, built by
+def truncation_bound_native(qa, sa, qw, sw, rowscaled=False):
+    """truncation_bound, evaluated by the plain C loop of
+    oracle/truncation_bound.c (oracle/libtbound.so, built by
     __graft_entry__.build(), or on first use) for full-size matrices;
     bit-identical to truncation_bound (every chunk's sum of lost terms is
-    exact in double)."""
+    exact in double).  rowscaled: sw is [K/128][N] as in truncation_bound."""
     import ctypes
     from . import native
     fn = native.load().fp8q_oracle_truncation_bound
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    fn.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, vp]
     fn.restype = None
     qa = np.ascontiguousarray(qa, dtype=np.uint8)
     qw = np.ascontiguousarray(qw, dtype=np.uint8)
@@ -176,12 +176,13 @@ def truncation_bound_native(qa, sa, qw, sw):
     sw = np.ascontiguousarray(sw, dtype=np.float32)
     M, K = qa.shape
     N = qw.shape[0]
+    sw_shape = (K // GROUP, N) if rowscaled else (N // GROUP, K // GROUP)
     if (qw.shape[1] != K or K % GROUP or N % GROUP or sa.shape != (K // GROUP, M)
-            or sw.shape != (N // GROUP, K // GROUP)):
+            or sw.shape != sw_shape):
         raise ValueError("truncation_bound_native: operand shapes do not match")
     out = np.empty((M, N), dtype=np.float64)
     fn(qa.ctypes.data, sa.ctypes.data, qw.ctypes.data, sw.ctypes.data, M, N, K,
-       out.ctypes.data)
+       1 if rowscaled else 0, out.ctypes.data)
     return out
 
 

@@ -54,8 +54,8 @@ def assert_gemm_bounded(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=Fal
     in units of its FP32 rounding bound (reported, not asserted).
     ref / absb: oracle.gemm and oracle.abs_bound of these operands, when the
     caller has them already.  native: T from the oracle's C evaluation
-    (mfma_model.truncation_bound_native, block-scaled operands), for bounds
-    over whole full-size outputs.
+    (mfma_model.truncation_bound_native), for bounds over whole full-size
+    outputs.
     """
     from oracle import mfma_model
     if ref is None or absb is None:
@@ -81,8 +81,7 @@ def assert_gemm_bounded(c_gpu, qa, sa, qw, sw, out="f32", what="", rowscaled=Fal
                                                (cols.reshape(-1, 128) // 128)[:, :1])
         sw_c = sw[cols[::128] // 128]
     if native:
-        assert not rowscaled, "the C evaluation covers block-scaled operands"
-        T = mfma_model.truncation_bound_native(qa, sa, qw[cols], sw_c)
+        T = mfma_model.truncation_bound_native(qa, sa, qw[cols], sw_c, rowscaled)
     else:
         T = mfma_model.truncation_bound(qa, sa, qw[cols], sw_c, rowscaled)
     fp32 = (G + 20) * mfma_model.U32 * absb[:, cols]

@@ -1,5 +1,5 @@
-"""Every output of the dense and decode workloads at full size against the
-exact oracle, through the C ABI.
+"""Every output of the dense and decode workloads at full size, and of the
+dense layer's two backward GEMMs, against the exact oracle, through the C ABI.
 
 - The quantizers' codes and scales are bit-exact on every row of the
   workloads' activations and weights.
@@ -101,3 +101,68 @@ def test_decode_workload_every_output():
         total += ref.size
     print(f"decode: {total} outputs; precise max err / tolerance {worst:.3g}; fast path max "
           f"err / its bound {worst_fast:.3g}, within 1e-5*sum|a||b|: {within / total:.6f}")
+
+
+def _layer_backward_inputs():
+    """The dense layer's backward operands: X and W of the dense workload
+    (4096 tokens x 7168, 4096 x 7168) and an upstream gradient dY of 4096 x
+    4096, N(0, 0.01^2) (seed 22, as the Wgrad test of test_gpu_backward)."""
+    X, W = workloads.dense_inputs("dense")
+    M, N = X.shape[0], W.shape[0]
+    dY = workloads.bf16_bits(
+        (np.random.default_rng(22).standard_normal((M, N)) * 1e-2).astype(np.float32))
+    return X, W, dY
+
+
+def test_dgrad_dense_layer_every_output():
+    """dX = dY W (4096 x 7168, inner dimension 4096): fp8q_gemm and
+    fp8q_gemm_precise on quantize_act(dY) and quantize_weight_t(W), every
+    output, against the oracle composed the same way."""
+    X, W, dY = _layer_backward_inputs()
+    print(f"\ndgrad {dY.shape[0]}x{W.shape[1]}x{dY.shape[1]}", flush=True)
+    f = fq()
+    qd, sd = f.quantize_act(to_dev_bf16(dY))
+    qwt, swt = f.quantize_weight_t(to_dev_bf16(W))
+    dx = f.gemm(qd, sd, qwt, swt)
+    dxp = f.gemm(qd, sd, qwt, swt, precise=True)
+    torch.cuda.synchronize()
+    od = oquant.quantize_act(dY)
+    owt = oquant.quantize_weight_t(W)
+    assert np.array_equal(host(qd), od[0]) and np.array_equal(host(sd).view(np.uint32),
+                                                              od[1].view(np.uint32))
+    assert np.array_equal(host(qwt), owt[0]) and np.array_equal(host(swt).view(np.uint32),
+                                                                owt[1].view(np.uint32))
+    ref = ogemm.gemm(*od, *owt)
+    absb = ogemm.abs_bound(*od, *owt)
+    rp = assert_gemm_strict(_f64(dxp), *od, *owt, what="dgrad precise, every output",
+                            ref=ref, absb=absb)
+    rf = assert_gemm_bounded(_f64(dx), *od, *owt, what="dgrad fast path, every output",
+                             ref=ref, absb=absb, native=True)
+    print(f"dgrad precise: {rp}; fast path: {rf}")
+
+
+def test_wgrad_dense_layer_every_output():
+    """dW = dY^T X (4096 x 7168, inner dimension the 4096 tokens):
+    fp8q_gemm_rowscaled and fp8q_gemm_rowscaled_precise on quantize_act_t(dY)
+    and quantize_act_t(X), every output, against the oracle composed the same
+    way (row-group scales on both operands)."""
+    X, W, dY = _layer_backward_inputs()
+    print(f"\nwgrad {dY.shape[1]}x{X.shape[1]}x{dY.shape[0]}", flush=True)
+    f = fq()
+    qdt, sdt = f.quantize_act_t(to_dev_bf16(dY))
+    qxt, sxt = f.quantize_act_t(to_dev_bf16(X))
+    dw = f.gemm_rowscaled(qdt, sdt, qxt, sxt)
+    dwp = f.gemm_rowscaled(qdt, sdt, qxt, sxt, precise=True)
+    torch.cuda.synchronize()
+    odt = oquant.quantize_act_t(dY)
+    oxt = oquant.quantize_act_t(X)
+    for (q, s), (oq, os_) in (((qdt, sdt), odt), ((qxt, sxt), oxt)):
+        assert np.array_equal(host(q), oq) and np.array_equal(host(s).view(np.uint32),
+                                                              os_.view(np.uint32))
+    ref = ogemm.gemm_rowscaled(*odt, *oxt)
+    absb = ogemm.abs_bound_rowscaled(*odt, *oxt)
+    rp = assert_gemm_strict(_f64(dwp), *odt, *oxt, what="wgrad precise, every output",
+                            rowscaled=True, ref=ref, absb=absb)
+    rf = assert_gemm_bounded(_f64(dw), *odt, *oxt, what="wgrad fast path, every output",
+                             rowscaled=True, ref=ref, absb=absb, native=True)
+    print(f"wgrad precise: {rp}; fast path: {rf}")

@@ -226,13 +226,29 @@ def _native_cases():
 
 def test_truncation_bound_native_equals_numpy():
     """The plain C evaluation (oracle/truncation_bound.c) reproduces the NumPy
-    truncation_bound bit for bit on every output."""
+    truncation_bound bit for bit on every output, with block-scaled weights
+    and with row-group scales on the second operand (1x128 groups along K of
+    each of its rows, as the weight-gradient GEMM has)."""
+    rng = np.random.default_rng(32)
     for qa, sa, qw, sw in _native_cases():
         T = mfma_model.truncation_bound(qa, sa, qw, sw)
         Tn = mfma_model.truncation_bound_native(qa, sa, qw, sw)
         assert T.shape == Tn.shape
         assert np.array_equal(T.view(np.uint64), Tn.view(np.uint64))
         assert (T > 0).any()
+        N, K = qw.shape
+        sb = rng.uniform(0.25, 4.0, size=(K // 128, N)).astype(np.float32)
+        Tr = mfma_model.truncation_bound(qa, sa, qw, sb, rowscaled=True)
+        Trn = mfma_model.truncation_bound_native(qa, sa, qw, sb, rowscaled=True)
+        assert np.array_equal(Tr.view(np.uint64), Trn.view(np.uint64))
+        # the row-group scales are indexed [chunk][column]: zeroing chunk 0's
+        # scales gives the bound of the operands without chunk 0
+        sb0 = sb.copy()
+        sb0[0] = 0.0
+        T0 = mfma_model.truncation_bound_native(qa, sa, qw, sb0, rowscaled=True)
+        T1 = mfma_model.truncation_bound_native(qa[:, 128:], sa[1:], qw[:, 128:], sb[1:],
+                                                rowscaled=True)
+        assert np.array_equal(T0, T1)
 
 
 def test_truncation_bound_native_hand_cases():
@@ -260,3 +276,8 @@ def test_truncation_bound_native_rejects_mismatched_shapes():
                       (ok_sa, ok_sw, np.zeros((128, 384), np.uint8))):  # K
         with pytest.raises(ValueError):
             mfma_model.truncation_bound_native(qa, sa, w, sw)
+    # row-scaled: sw is [K/128][N]
+    assert mfma_model.truncation_bound_native(qa, ok_sa, qw, np.ones((2, 128), np.float32),
+                                              rowscaled=True).shape == (2, 128)
+    with pytest.raises(ValueError):
+        mfma_model.truncation_bound_native(qa, ok_sa, qw, ok_sw, rowscaled=True)
